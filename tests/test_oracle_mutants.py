@@ -1,0 +1,71 @@
+"""Planted mistakes: each mutant is a copy of oracle.c with one plausible error (a dropped
+term, a wrong sign, a wrong index, a transposed operand...).  Built on the CPU into a
+temporary directory and run against the pins, every mutant must fail at least one pin.
+This shows the pins constrain every function of the oracle, not just that it agrees with
+itself."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "causal_drops_diagonal": ("int n = causal ? i + 1 : N;", "int n = causal ? i : N;"),
+    "online_skips_rescale": ("for (int c = 0; c < dv; ++c) acc[c] *= corr;",
+                             "for (int c = 0; c < dv; ++c) acc[c] *= 1.0;"),
+    "lse_wrong_sign": ("*lse = m + log(l);", "*lse = m - log(l);"),
+    "gqa_wrong_head_map": ("int kvh = h / group;\n                const uint16_t* kbase",
+                           "int kvh = h % Hkv;\n                const uint16_t* kbase"),
+    "k_and_v_swapped": ("kr[j] = kbase + (int64_t)j * d;\n                    vr[j] = vbase",
+                        "kr[j] = vbase + (int64_t)j * d;\n                    vr[j] = kbase"),
+    "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "merge_weight_inverted": ("double w = exp(lse_s[s] - M);", "double w = exp(M - lse_s[s]);"),
+    "decode_wrong_slot": ("int slot = tok % page_size;", "int slot = (tok + 1) % page_size;"),
+    "fp16_wrong_bias": ("expo - 25);", "expo - 24);"),
+    "online_l_not_rescaled": ("l = l * corr + rowsum;", "l = l + rowsum;"),
+    "softmax_not_normalised": ("s[j] = s[j] / l;   /* P_ij */", "s[j] = s[j];"),
+}
+
+PINS = [
+    lambda: pins.test_widen16_matches_numpy_for_every_pattern(pins.FP16),
+    pins.test_single_visible_key_returns_v_bits_exactly,
+    pins.test_three_scores_two_tiles_zwjcode_section04,
+    pins.test_rechunk_lse_and_weights_llm_internals_10_3_2,
+    pins.test_element_stream_cs349d_exercise1,
+    pins.test_split_merge_max_refresh_handbook_exercise1,
+    lambda: pins.test_attention_matches_torch_sdpa_float64(2, 4, 2, 37, 16, True, pins.BF16),
+    lambda: pins.test_attention_matches_torch_sdpa_float64(1, 3, 1, 50, 8, True, pins.FP16),
+    pins.test_scale_is_applied_to_scores_not_values,
+    lambda: pins.test_tiled_online_equals_library_softmax(257, 16),
+    lambda: pins.test_merge_is_order_free(8),
+    pins.test_bsr_example_paged_equals_contiguous_exactly,
+    pins.test_decode_matches_torch_sdpa_and_is_page_order_free,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_fails_a_pin(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    str(mut), "-o", str(lib), "-lm"], check=True)
+    failed = []
+    oracle.use_library(str(lib))
+    try:
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError):
+                failed.append(pin)
+    finally:
+        oracle.use_library(None)
+    assert failed, f"mutant {name} passed every pin"

@@ -1,0 +1,363 @@
+"""Pins for the fp64 oracle: it is tied here to things other than itself.
+
+* the pages' worked examples (tests/golden/*.json, each with its citation);
+* closed forms (zero queries give uniform attention; a single visible key; constant V);
+* library routines: torch's float64 CPU scaled_dot_product_attention (math path, with its
+  own causal mask, scale and GQA expansion), scipy's softmax / logsumexp, numpy's 16-bit
+  conversions;
+* invariants the pages state: tiled equals untiled, the merge is order-free, paged equals
+  contiguous exactly, rows of P sum to 1.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special as sps
+import torch
+import torch.nn.functional as F
+
+import oracle
+from attn_inputs import (BF16, FP16, bits_to_f64, decode_case, f32_to_bf16_bits, normal_bits,
+                         permute_pages, prefill_case)
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def half_ulp(printed: str) -> float:
+    """Half a unit in the last printed digit."""
+    s = str(printed)
+    dec = len(s.split(".")[1]) if "." in s else 0
+    return 0.5 * 10.0 ** (-dec)
+
+
+def close_printed(value, printed, tol=None):
+    t = half_ulp(printed) if tol is None else tol
+    assert abs(value - float(printed)) <= t + 1e-12, (value, printed, t)
+
+
+def bf16(vals):
+    return f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def scores_as_attention(scores, values, causal=False):
+    """A one-dimensional attention problem whose every row has the given scores:
+    d = 1, q = 1, k_j = score_j, v_j = value_j, scale = 1 (all exact in bf16)."""
+    n = len(scores)
+    q = bf16(np.ones(n)).reshape(1, 1, n, 1)
+    k = bf16(scores).reshape(1, 1, n, 1)
+    v = bf16(values).reshape(1, 1, n, 1)
+    return q, k, v
+
+
+# ----------------------------------------------------------------------------- 16-bit widening
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+def test_widen16_matches_numpy_for_every_pattern(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        ref = bits_to_f64(bits, dtype)
+    got = np.array([oracle.widen16(int(b), dtype) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_single_visible_key_returns_v_bits_exactly():
+    # O of a row with one visible key is that key's V row, widened exactly
+    for dtype in (BF16, FP16):
+        v = normal_bits((1, 1, 1, 64), 5, dtype)
+        O, L = oracle.attention(np.zeros_like(v), np.zeros_like(v), v, causal=True, scale=1.0,
+                                dtype=dtype)
+        assert np.array_equal(O.reshape(-1), bits_to_f64(v.reshape(-1), dtype))
+        assert L.reshape(-1)[0] == 0.0
+
+
+# ----------------------------------------------------------------------------- worked examples
+def test_three_scores_two_tiles_zwjcode_section04():
+    g = gold("online_softmax_three_scores.json")
+    r = oracle.online_row(g["scores"], g["values"], bc=2)
+    for t, st in enumerate(g["after_tile"]):
+        assert r["trace_m"][t] == st["m"]
+        close_printed(r["trace_l"][t], st["l"])
+        close_printed(r["trace_acc"][t, 0], st["acc"])
+    close_printed(r["O"][0], g["output"])
+    # the same numbers through the standard (untiled) oracle: every row of the 1-d problem
+    q, k, v = scores_as_attention(g["scores"], g["values"])
+    O, L = oracle.attention(q, k, v, causal=False, scale=1.0, dtype=BF16)
+    for i in range(3):
+        close_printed(O[0, 0, i, 0], g["output"])
+        assert abs(O[0, 0, i, 0] - r["O"][0]) < 1e-12
+        close_printed(math.exp(L[0, 0, i] - 3.0), g["after_tile"][-1]["l"])
+
+
+def test_rechunk_lse_and_weights_llm_internals_10_3_2():
+    g = gold("online_softmax_rechunk.json")
+    for key in ("order_a", "order_b"):
+        c = g[key]
+        r = oracle.online_row(c["scores"], c["values"], bc=c["tile"])
+        for t, st in enumerate(c["after_tile"]):
+            assert r["trace_m"][t] == st["m"]
+            close_printed(r["trace_l"][t], st["l"])
+            close_printed(r["trace_acc"][t, 0], st["acc"])
+        close_printed(r["O"][0], g["output"])
+        close_printed(r["lse"], g["lse"])
+    q, k, v = scores_as_attention(g["order_a"]["scores"], g["order_a"]["values"])
+    O, L, P = oracle.attention(q, k, v, causal=False, scale=1.0, dtype=BF16, return_probs=True)
+    close_printed(O[0, 0, 0, 0], g["output"])
+    close_printed(L[0, 0, 0], g["lse"])
+    for w, pw in zip(P[0, 0, 0], g["weights_for_scores_1_3_2"]):
+        close_printed(w, pw)
+    # LSE merge of the two chunks [1,3] and [2]: ln(e^L1 + e^L2), weights e^(Lk - L)
+    a = oracle.online_row([1, 3], [10, 20], bc=2)
+    b = oracle.online_row([2], [30], bc=1)
+    Om, Lm = oracle.merge([a["O"], b["O"]], [a["lse"], b["lse"]])
+    close_printed(Om[0], g["output"])
+    close_printed(Lm, g["lse"])
+
+
+def test_element_stream_cs349d_exercise1():
+    g = gold("online_softmax_element_stream.json")
+    r = oracle.online_row(g["scores"], np.zeros(3), bc=1)
+    for t, st in enumerate(g["after_tile"]):
+        assert r["trace_m"][t] == st["m"]
+        close_printed(r["trace_l"][t], st["l"])
+    close_printed(r["trace_l"][1] * math.exp(2 - 4), g["rescaled_l_before_last_add"])
+    q, k, v = scores_as_attention(g["scores"], [0, 0, 0])
+    O, L, P = oracle.attention(q, k, v, causal=False, scale=1.0, dtype=BF16, return_probs=True)
+    for w, pw in zip(P[0, 0, 0], g["softmax"]):
+        close_printed(w, pw)
+
+
+def test_split_merge_max_refresh_handbook_exercise1():
+    g = gold("split_merge_max_refresh.json")
+    s = sum((b["scores"] for b in g["blocks"]), [])
+    v = sum((b["values"] for b in g["blocks"]), [])
+    r = oracle.online_row(s, v, bc=2)
+    for t, st in enumerate(g["after_block"]):
+        assert r["trace_m"][t] == st["m"]
+        close_printed(r["trace_l"][t], st["l"])
+        close_printed(r["trace_acc"][t, 0], st["acc"], st.get("acc_tol"))
+    close_printed(math.exp(r["trace_m"][0] - r["trace_m"][1]), g["correction_second_block"])
+    close_printed(r["O"][0], g["output"])
+    # split-K form: each block normalised on its own, merged by the LSE rule
+    parts = [oracle.online_row(b["scores"], b["values"], bc=len(b["scores"])) for b in g["blocks"]]
+    Om, Lm = oracle.merge([p["O"] for p in parts], [p["lse"] for p in parts])
+    close_printed(Om[0], g["output"])
+    # direct: weights proportional to e^score
+    q, k, vv = scores_as_attention(s, v)
+    O, L = oracle.attention(q, k, vv, causal=False, scale=1.0, dtype=BF16)
+    close_printed(O[0, 0, 0, 0], g["output"])
+    for sc, pw in zip(s, g["direct_weights_unnormalised"]):
+        close_printed(math.exp(sc), pw)
+    close_printed(math.exp(L[0, 0, 0]), g["direct_weight_sum"])
+
+
+# ----------------------------------------------------------------------------- library cross-checks
+def _sdpa_ref(case, causal):
+    q = torch.from_numpy(bits_to_f64(case.q, case.dtype))
+    k = torch.from_numpy(bits_to_f64(case.k, case.dtype))
+    v = torch.from_numpy(bits_to_f64(case.v, case.dtype))
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=case.scale,
+                                       enable_gqa=case.Hq != case.Hkv)
+    # LSE through scipy: scores by a library matmul, masked, logsumexp
+    rep = case.Hq // case.Hkv
+    kk = np.repeat(bits_to_f64(case.k, case.dtype), rep, axis=1)
+    s = case.scale * np.matmul(bits_to_f64(case.q, case.dtype), np.swapaxes(kk, -1, -2))
+    if causal:
+        n = s.shape[-1]
+        s = np.where(np.tril(np.ones((n, n), bool)), s, -np.inf)
+    return o.numpy(), sps.logsumexp(s, axis=-1)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,dtype", [
+    (2, 4, 2, 37, 16, True, BF16),
+    (2, 4, 2, 37, 16, False, BF16),
+    (1, 3, 1, 50, 8, True, FP16),
+    (1, 2, 2, 1, 64, True, BF16),
+    (3, 8, 8, 20, 32, False, FP16),
+])
+def test_attention_matches_torch_sdpa_float64(B, Hq, Hkv, N, d, causal, dtype):
+    case = prefill_case(B, Hq, Hkv, N, d, causal, dtype, seeds=(11, 12, 13))
+    O, L = oracle.attention(case.q, case.k, case.v, causal, case.scale, dtype)
+    o_ref, l_ref = _sdpa_ref(case, causal)
+    np.testing.assert_allclose(O, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L, l_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_scale_is_applied_to_scores_not_values():
+    case = prefill_case(1, 2, 1, 9, 16, False, BF16, scale=0.37, seeds=(21, 22, 23))
+    O, L = oracle.attention(case.q, case.k, case.v, False, case.scale, BF16)
+    o_ref, l_ref = _sdpa_ref(case, False)
+    np.testing.assert_allclose(O, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L, l_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_row_subset_equals_full_evaluation():
+    case = prefill_case(2, 4, 2, 33, 16, True, BF16, seeds=(31, 32, 33))
+    O, L = oracle.attention(case.q, case.k, case.v, True, case.scale, BF16)
+    rows = np.array([0, 5, 32, 33 * 4 + 7, 2 * 4 * 33 - 1], dtype=np.int64)
+    Os, Ls = oracle.attention(case.q, case.k, case.v, True, case.scale, BF16, rows=rows)
+    assert np.array_equal(Os, O.reshape(-1, 16)[rows])
+    assert np.array_equal(Ls, L.reshape(-1)[rows])
+
+
+# ----------------------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("causal", [True, False])
+def test_zero_queries_give_uniform_attention(causal):
+    case = prefill_case(1, 2, 1, 40, 16, causal, BF16, seeds=(41, 42, 43))
+    q0 = np.zeros_like(case.q)
+    O, L = oracle.attention(q0, case.k, case.v, causal, case.scale, BF16)
+    v = bits_to_f64(case.v, BF16)[0, 0]
+    for i in range(40):
+        n = i + 1 if causal else 40
+        np.testing.assert_allclose(O[0, 1, i], v[:n].mean(axis=0), rtol=1e-13, atol=1e-14)
+        assert abs(L[0, 1, i] - math.log(n)) < 1e-14
+
+
+def test_single_visible_key_and_constant_values():
+    case = prefill_case(1, 1, 1, 16, 32, True, BF16, seeds=(51, 52, 53))
+    O, L = oracle.attention(case.q, case.k, case.v, True, case.scale, BF16)
+    v = bits_to_f64(case.v, BF16)[0, 0]
+    assert np.array_equal(O[0, 0, 0], v[0])        # row 0 sees only key 0: P = 1 exactly
+    s00 = case.scale * np.dot(bits_to_f64(case.q, BF16)[0, 0, 0], bits_to_f64(case.k, BF16)[0, 0, 0])
+    assert abs(L[0, 0, 0] - s00) < 1e-14
+    vc = np.full_like(case.v, f32_to_bf16_bits(np.array([1.5], np.float32))[0])
+    O2, _ = oracle.attention(case.q, case.k, vc, True, case.scale, BF16)
+    np.testing.assert_allclose(O2, 1.5, rtol=1e-14, atol=0)
+
+
+def test_rows_of_p_sum_to_one_and_masked_entries_are_zero():
+    case = prefill_case(1, 2, 2, 30, 16, True, BF16, seeds=(61, 62, 63))
+    _, _, P = oracle.attention(case.q, case.k, case.v, True, case.scale, BF16, return_probs=True)
+    assert np.all(np.abs(P.sum(-1) - 1.0) <= 1e-14)
+    assert np.all(P[..., np.triu_indices(30, 1)[0], np.triu_indices(30, 1)[1]] == 0)
+    assert np.all(P >= 0)
+
+
+def test_gqa_equals_replicated_mha():
+    case = prefill_case(2, 8, 2, 25, 16, True, BF16, seeds=(71, 72, 73))
+    O, L = oracle.attention(case.q, case.k, case.v, True, case.scale, BF16)
+    k_rep = np.repeat(case.k, 4, axis=1)
+    v_rep = np.repeat(case.v, 4, axis=1)
+    O2, L2 = oracle.attention(case.q, k_rep, v_rep, True, case.scale, BF16)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+# ----------------------------------------------------------------------------- tiled = untiled, merge
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 64, 257, 1000])
+@pytest.mark.parametrize("bc", [1, 2, 3, 16, 64])
+def test_tiled_online_equals_library_softmax(n, bc):
+    rng = np.random.default_rng(1000 + n * 7 + bc)
+    s = rng.standard_normal(n) * 3.0
+    v = rng.standard_normal((n, 5))
+    r = oracle.online_row(s, v, bc)
+    ref = sps.softmax(s) @ v
+    np.testing.assert_allclose(r["O"], ref, rtol=1e-12, atol=1e-13)
+    assert abs(r["lse"] - sps.logsumexp(s)) <= 1e-12 * max(1.0, abs(r["lse"]))
+    assert r["m"] == s.max()
+
+
+def test_online_row_with_masked_scores():
+    s = np.array([-np.inf, 0.5, -np.inf, 2.0, -np.inf])
+    v = np.arange(10.0).reshape(5, 2)
+    r = oracle.online_row(s, v, bc=2)       # first tile holds one visible score
+    ref = sps.softmax(s) @ v
+    np.testing.assert_allclose(r["O"], ref, rtol=1e-14)
+    r2 = oracle.online_row(np.full(3, -np.inf), np.ones((3, 1)), bc=2)
+    assert r2["lse"] == -np.inf and r2["O"][0] == 0.0
+
+
+@pytest.mark.parametrize("segments", [2, 8, 64])
+def test_merge_is_order_free(segments):
+    rng = np.random.default_rng(segments)
+    n = 10000
+    s = rng.standard_normal(n) * 2.0
+    v = rng.standard_normal((n, 3))
+    cuts = np.sort(rng.choice(np.arange(1, n), segments - 1, replace=False))
+    bounds = np.concatenate([[0], cuts, [n]])
+    parts = [oracle.online_row(s[a:b], v[a:b], bc=64) for a, b in zip(bounds[:-1], bounds[1:])]
+    O_s = np.array([p["O"] for p in parts])
+    L_s = np.array([p["lse"] for p in parts])
+    ref = sps.softmax(s) @ v
+    for order in (np.arange(segments), np.arange(segments)[::-1], rng.permutation(segments)):
+        Om, Lm = oracle.merge(O_s[order], L_s[order])
+        np.testing.assert_allclose(Om, ref, rtol=1e-13, atol=1e-14)
+        assert abs(Lm - sps.logsumexp(s)) < 1e-12
+    # an empty part (LSE = -inf) carries weight 0
+    Om, Lm = oracle.merge(np.vstack([O_s, np.full((1, 3), 123.0)]), np.append(L_s, -np.inf))
+    np.testing.assert_allclose(Om, ref, rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- paged decode
+def test_bsr_example_paged_equals_contiguous_exactly():
+    g = gold("bsr_page_table_example.json")
+    lengths, tables, ps = g["lengths"], g["tables"], g["page_size"]
+    # the printed BSR arrays are the concatenated tables and their prefix counts
+    assert sum(tables, []) == g["indices"]
+    assert list(np.cumsum([0] + [len(t) for t in tables])) == g["indptr"]
+    assert [len(t) for t in tables] == [-(-n // ps) for n in lengths]
+    B, Hq, Hkv, d = 3, 4, 2, 8
+    num_pages = max(g["indices"]) + 1
+    table = np.full((B, max(len(t) for t in tables)), -1, np.int32)
+    for r, t in enumerate(tables):
+        table[r, :len(t)] = t
+    q = normal_bits((B, Hq, d), 81, BF16)
+    kp = normal_bits((num_pages, ps, Hkv, d), 82, BF16)
+    vp = normal_bits((num_pages, ps, Hkv, d), 83, BF16)
+    O, L = oracle.decode_paged(q, kp, vp, table, lengths, 0.3, BF16)
+    for r in range(B):
+        n = lengths[r]
+        toks = np.arange(n)
+        pages = table[r, toks // ps]
+        kc = kp[pages, toks % ps]            # [n, Hkv, d] gathered, contiguous
+        vc = vp[pages, toks % ps]
+        # decode of request r = last row of a causal prefill whose last query is q_r
+        qq = np.zeros((1, Hq, n, d), np.uint16)
+        qq[0, :, n - 1] = q[r]
+        Oc, Lc = oracle.attention(qq, np.ascontiguousarray(kc.transpose(1, 0, 2))[None],
+                                  np.ascontiguousarray(vc.transpose(1, 0, 2))[None], True, 0.3, BF16)
+        assert np.array_equal(O[r], Oc[0, :, n - 1])   # max difference exactly 0
+        assert np.array_equal(L[r], Lc[0, :, n - 1])
+
+
+def test_decode_matches_torch_sdpa_and_is_page_order_free():
+    case = decode_case(5, 8, 2, 32, [1, 17, 100, 33, 64], page_size=16, seeds=(91, 92, 93))
+    O, L = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                               case.ctx_lens, case.scale, BF16)
+    for r in range(case.B):
+        n = int(case.ctx_lens[r])
+        toks = np.arange(n)
+        pages = case.block_table[r, toks // 16]
+        kc = bits_to_f64(case.k_pages[pages, toks % 16], BF16).transpose(1, 0, 2)[None]
+        vc = bits_to_f64(case.v_pages[pages, toks % 16], BF16).transpose(1, 0, 2)[None]
+        qv = bits_to_f64(case.q[r], BF16)[None, :, None, :]
+        o = F.scaled_dot_product_attention(torch.from_numpy(qv), torch.from_numpy(kc),
+                                           torch.from_numpy(vc), scale=case.scale, enable_gqa=True)
+        np.testing.assert_allclose(O[r], o.numpy()[0, :, 0], rtol=1e-12, atol=1e-12)
+        s = case.scale * np.einsum("hd,hnd->hn", bits_to_f64(case.q[r], BF16),
+                                   np.repeat(kc[0], 4, axis=0))
+        np.testing.assert_allclose(L[r], sps.logsumexp(s, axis=-1), rtol=1e-12, atol=1e-12)
+    perm = permute_pages(case, 1234)
+    O2, L2 = oracle.decode_paged(perm.q, perm.k_pages, perm.v_pages, perm.block_table,
+                                 perm.ctx_lens, perm.scale, BF16)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_decode_zero_queries_count_visible_tokens():
+    case = decode_case(4, 4, 1, 16, [1, 15, 16, 300], page_size=16, seeds=(94, 95, 96))
+    O, L = oracle.decode_paged(np.zeros_like(case.q), case.k_pages, case.v_pages,
+                               case.block_table, case.ctx_lens, case.scale, BF16)
+    assert np.array_equal(np.round(np.exp(L)), np.repeat(case.ctx_lens[:, None], 4, 1).astype(float))
+
+
+def test_decode_empty_context_reading():
+    case = decode_case(2, 2, 1, 8, [0, 5], page_size=16, seeds=(97, 98, 99))
+    O, L = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                               case.ctx_lens, case.scale, BF16)
+    assert np.all(L[0] == -np.inf) and np.all(O[0] == 0.0) and np.all(np.isfinite(L[1]))
