@@ -1,0 +1,53 @@
+// attn_internal.h -- launcher interface between the C ABI shim and the kernels.
+// Arguments reaching these launchers have already been validated by the shim.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+struct PrefillArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* O;
+    float* LSE;
+    int B, Hq, Hkv, N, d;
+    bool causal, is_bf16;
+    float scale;
+    void* stream;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* Kpages;
+    const void* Vpages;
+    const int* block_table;
+    const int* ctx_lens;
+    void* O;
+    float* LSE;  // may be null
+    int B, Hq, Hkv, d, page_size, max_pages, split_tokens;
+    bool is_bf16;
+    float scale;
+    void* workspace;
+    void* stream;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Number of splits per sequence the workspace is sized for.
+inline long long decode_max_splits(int page_size, int max_pages, int split_tokens) {
+    const long long max_tokens = (long long)max_pages * page_size;
+    return (max_tokens + split_tokens - 1) / split_tokens;
+}
+
+// Workspace layout: O partials [B][Hq][S][d] fp32, then LSE partials [B][Hq][S] fp32.
+inline size_t decode_workspace_bytes(int B, int Hq, int d, long long S) {
+    const size_t o = (size_t)B * Hq * (size_t)S * d * sizeof(float);
+    const size_t l = (size_t)B * Hq * (size_t)S * sizeof(float);
+    return o + ((l + 255) / 256) * 256;
+}
+
+}  // namespace attn

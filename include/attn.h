@@ -1,0 +1,133 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
+ *
+ * Two compute calls follow the problem statement of the pages:
+ *   attn_fwd           exact scaled-dot-product attention forward (prefill), computed as a
+ *                      tiled, fused kernel with online softmax: Q row-blocks stay on chip
+ *                      while K/V column-blocks stream past, fully masked causal blocks are
+ *                      skipped, and only O and the per-row LSE are written.
+ *                      [LLM Internals 10.3.2, tiled forward in FlashAttention-2 loop order,
+ *                      with "write back O_i = O~/l, LSE_i = m + ln l"; CS349D Lecture 4
+ *                      notes 3.2-3.3; zwjcode.cn FlashAttention blog sections 02-06]
+ *   attn_decode_paged  one query token per sequence against a paged KV cache, split along
+ *                      the keys (Flash-Decoding / split-KV); each split writes a partial
+ *                      state and the splits are merged with the LSE rule.
+ *                      [CS349D Lecture 4 notes 4.2-4.3; LLM Internals 10.3.7; AI-infra
+ *                      handbook "FlashAttention and inference operators", Flash-Decoding
+ *                      split-K merge and the paged GQA decode kernel]
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees, copies to the host or synchronises.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the null stream) and is asynchronous: read results only after
+ *     synchronising that stream.
+ *   - Every argument is validated on the host before any HIP call; on error nothing is
+ *     launched and nothing is written.  There is no fallback path: an unsupported input is
+ *     an error, never a silent switch to slower code.
+ *   - Device-resident block tables and context lengths are not read on the host and are
+ *     not validated (see attn_decode_paged).
+ *   - Results are bitwise deterministic for fixed inputs, shapes and split size: there are
+ *     no atomics and all reductions run in a fixed order.
+ *   - The library keeps no state between calls and may be called from several host
+ *     threads on different streams.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (return values). */
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,        /* a required pointer is NULL                                  */
+    ATTN_ERR_SHAPE = -2,       /* a size is <= 0, Hq % Hkv != 0, sizes overflow, or scale is   */
+                               /* not a finite positive number                                */
+    ATTN_ERR_DTYPE = -3,       /* dtype is neither ATTN_BF16 nor ATTN_FP16                     */
+    ATTN_ERR_UNSUPPORTED = -4, /* valid attention, but not built here: d not in {64, 128},     */
+                               /* page_size != 16, split_tokens not a positive multiple of     */
+                               /* page_size                                                    */
+    ATTN_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned                      */
+    ATTN_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the helper's size             */
+    ATTN_ERR_HIP = -7          /* the HIP runtime reported an error at launch                  */
+};
+
+/* Element type of Q, K, V, O (and q, K/V pages, O for decode). */
+enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
+
+/*
+ * attn_fwd -- prefill / full attention forward.
+ *
+ *   Q   [B, Hq,  N, d]  dtype, contiguous          (read)
+ *   K   [B, Hkv, N, d]  dtype, contiguous          (read)
+ *   V   [B, Hkv, N, d]  dtype, contiguous          (read)
+ *   O   [B, Hq,  N, d]  dtype, contiguous          (written)
+ *   LSE [B, Hq,  N]     float32                     (written; natural log of the row's
+ *                        sum of exp(scale * q.k) over its visible keys)
+ *
+ *   O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:].K[b,kvh,j,:]) V[b,kvh,j,:]
+ *   with kvh = h / (Hq / Hkv) (query-head groups are contiguous) and, when causal != 0,
+ *   only keys j <= i visible.  Scores, statistics and accumulation are fp32; the
+ *   probabilities feeding the second product are rounded to dtype (round-to-nearest-even),
+ *   as is O.
+ *
+ *   Supported: d in {64, 128}; dtype bf16 or fp16; any N >= 1, B >= 1, Hq % Hkv == 0;
+ *   scale finite and > 0.  All five pointers must be 16-byte aligned.
+ *   Returns ATTN_OK or a negative attn_status.
+ */
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+             int dtype, void* stream);
+
+/*
+ * attn_decode_paged -- one query token per sequence over a paged KV cache, split-KV.
+ *
+ *   q            [B, Hq, d]                         dtype          (read)
+ *   Kpages       [num_pages, page_size, Hkv, d]     dtype          (read)
+ *   Vpages       [num_pages, page_size, Hkv, d]     dtype          (read)
+ *   block_table  [B, max_pages_per_seq]             int32, device  (read)
+ *   ctx_lens     [B]                                int32, device  (read)
+ *   O            [B, Hq, d]                         dtype          (written)
+ *   LSE          [B, Hq] float32, or NULL            (written when not NULL)
+ *   workspace    >= attn_decode_paged_workspace_bytes(...) bytes, 16-byte aligned,
+ *                device memory the library may overwrite (per-split partial states)
+ *
+ *   Token t of sequence r is slot t % page_size of physical page block_table[r][t /
+ *   page_size]; kv head kvh = h / (Hq / Hkv).  All ctx_lens[r] tokens are visible.  The
+ *   keys are cut into splits of split_tokens tokens starting at token 0; each split yields
+ *   a partial (O_s normalised, LSE_s), and the splits of a sequence are merged in
+ *   ascending order: LSE = ln sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.
+ *   A sequence with ctx_lens[r] == 0 gets O = 0 and LSE = -inf.
+ *
+ *   Caller preconditions (device data, not checked): 0 <= ctx_lens[r] <=
+ *   max_pages_per_seq * page_size, and every block_table entry a sequence uses
+ *   (index < ceil(ctx/page_size)) is a valid page in [0, num_pages).  Entries past that are
+ *   never read and may hold anything (e.g. -1).
+ *
+ *   Supported: d in {64, 128}; page_size == 16; split_tokens a positive multiple of
+ *   page_size; dtype bf16 or fp16; Hq % Hkv == 0 with Hq / Hkv <= 16.  q, Kpages, Vpages,
+ *   O and workspace must be 16-byte aligned; block_table, ctx_lens and LSE 4-byte aligned.
+ *   Returns ATTN_OK or a negative attn_status.
+ */
+int attn_decode_paged(const void* q, const void* Kpages, const void* Vpages,
+                      const int* block_table, const int* ctx_lens, void* O, float* LSE,
+                      int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                      int split_tokens, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_workspace_bytes -- host-only helper: the workspace attn_decode_paged
+ * needs for these sizes (partial outputs and LSEs of every split of every (sequence,
+ * head)).  Returns 0 when the sizes are invalid.  Makes no HIP call.
+ */
+size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int page_size,
+                                         int max_pages_per_seq, int split_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

@@ -1,0 +1,101 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol include/attn.h
+declares, and rejects bad arguments on the host with the documented status codes before
+any HIP call (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+attn = pytest.importorskip("exact_attention_08_amd")
+L = attn.lib()
+
+A = 0x10000          # a 16-byte aligned fake device address; never dereferenced here
+MIS = 0x10008        # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_two_calls_and_the_helper():
+    assert declared_functions() == sorted(attn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def status_codes():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_\w+)\s*=\s*(-?\d+)", text)}
+
+
+def test_status_codes_match_binding():
+    codes = status_codes()
+    for code, name in attn.STATUS.items():
+        assert codes[name] == code
+
+
+def fwd(Q=A, K=A, V=A, O=A, LSE=A, B=1, Hq=4, Hkv=2, N=16, d=64, causal=1, scale=0.125,
+        dtype=0):
+    return L.attn_fwd(Q, K, V, O, LSE, B, Hq, Hkv, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), -1), (dict(K=None), -1), (dict(V=None), -1), (dict(O=None), -1),
+    (dict(LSE=None), -1),
+    (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(d=0), -2),
+    (dict(Hq=6, Hkv=4), -2), (dict(N=-5), -2), (dict(scale=0.0), -2), (dict(scale=-1.0), -2),
+    (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(d=96), -4), (dict(d=256), -4), (dict(d=32), -4),
+    (dict(Q=MIS), -5), (dict(O=MIS), -5), (dict(LSE=A + 4), -5),
+])
+def test_attn_fwd_rejects_bad_arguments(kw, code):
+    assert fwd(**kw) == code
+
+
+def dec(q=A, K=A, V=A, bt=A, ctx=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, d=128, page=16, max_pages=8,
+        split=64, scale=0.1, dtype=0, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.attn_decode_paged_workspace_bytes(B, Hq, d, 16, max_pages, max(split, 16))
+    return L.attn_decode_paged(q, K, V, bt, ctx, O, LSE, B, Hq, Hkv, d, page, max_pages, split,
+                               scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(K=None), -1), (dict(V=None), -1), (dict(bt=None), -1),
+    (dict(ctx=None), -1), (dict(O=None), -1),
+    (dict(B=0), -2), (dict(Hq=7), -2), (dict(max_pages=0), -2), (dict(split=0), -2),
+    (dict(scale=0.0), -2), (dict(page=0), -2),
+    (dict(dtype=5), -3),
+    (dict(d=80), -4), (dict(page=32), -4), (dict(page=8), -4), (dict(split=24), -4),
+    (dict(Hq=64, Hkv=2), -4),
+    (dict(q=MIS), -5), (dict(K=MIS), -5), (dict(O=MIS), -5), (dict(bt=A + 2), -5),
+    (dict(LSE=A + 2), -5), (dict(ws=MIS), -5),
+    (dict(ws=None), -6), (dict(ws_bytes=100), -6),
+])
+def test_attn_decode_paged_rejects_bad_arguments(kw, code):
+    assert dec(**kw) == code
+
+
+def test_workspace_helper():
+    ws = L.attn_decode_paged_workspace_bytes
+    # C5-like: 64 sequences x 32 heads, up to 2048 pages of 16 tokens, 1024-token splits
+    S = (2048 * 16 + 1023) // 1024
+    o = 64 * 32 * S * 128 * 4
+    l = 64 * 32 * S * 4
+    assert ws(64, 32, 128, 16, 2048, 1024) == o + ((l + 255) // 256) * 256
+    assert ws(0, 32, 128, 16, 2048, 1024) == 0
+    assert ws(1, 1, 64, 16, 1, 16) >= 64 * 4 + 4

@@ -1,0 +1,157 @@
+"""GPU parity of attn_decode_paged against the fp64 oracle, through the C ABI binding.
+
+Covers the handbook's context lengths (1, 17, 1000, 4096: a single token, a partial page),
+GQA, both dtypes and both head sizes; split-count invariance; bit-exact block-table logic
+(the same KV under an identity table and a shuffled table gives bitwise-equal output);
+poisoned unused slots, unused pages and a guard page in front of the pool; the zero-query
+count test; an empty context; and the full-size 64-sequence workload on sampled heads.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attn_inputs import BF16, FP16, CONFIGS, config_case, decode_case, permute_pages
+from tests.gpu_util import assert_parity, bits_of, from_dev_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC1
+NAN_F16 = 0x7E01
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_decode(case, split, q_bits=None, k_pages=None, v_pages=None, pool_offset=0,
+               want_lse=True):
+    """pool_offset: number of extra (guard) pages placed in front of the pool; the table
+    still indexes from the pool base."""
+    import exact_attention_08_amd as attn
+    kp = case.k_pages if k_pages is None else k_pages
+    vp = case.v_pages if v_pages is None else v_pages
+    Kall = to_dev(kp, case.dtype)
+    Vall = to_dev(vp, case.dtype)
+    K = Kall[pool_offset:]
+    V = Vall[pool_offset:]
+    q = to_dev(case.q if q_bits is None else q_bits, case.dtype)
+    bt = torch.from_numpy(case.block_table).cuda()
+    ctx = torch.from_numpy(case.ctx_lens).cuda()
+    O = torch.empty_like(q)
+    LSE = torch.empty(case.B, case.Hq, dtype=torch.float32, device="cuda") if want_lse else None
+    nbytes = attn.attn_decode_paged_workspace_bytes(case.B, case.Hq, case.d, case.page_size,
+                                                    case.max_pages, split)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    attn.attn_decode_paged(q, K, V, bt, ctx, O, LSE, split, ws, case.scale)
+    torch.cuda.synchronize()
+    return O, LSE
+
+
+@pytest.mark.parametrize("ctx,Hq,Hkv,d,dtype,split", [
+    ([1, 17, 1000, 4096], 32, 8, 128, BF16, 1024),     # the handbook's test lengths
+    ([1, 17, 1000, 4096], 32, 8, 128, FP16, 256),
+    ([5, 16, 33, 700], 8, 8, 64, BF16, 64),
+    ([2047, 48, 3000], 16, 1, 128, BF16, 512),
+    ([100, 1, 64, 65, 4100], 12, 4, 64, FP16, 16),
+])
+def test_decode_small_all_heads(ctx, Hq, Hkv, d, dtype, split):
+    say(f"decode small ctx{ctx} Hq{Hq} Hkv{Hkv} d{d} dtype{dtype} split{split}")
+    case = decode_case(len(ctx), Hq, Hkv, d, ctx, 16, dtype)
+    O, LSE = run_decode(case, split)
+    O_ref, L_ref = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                       case.ctx_lens, case.scale, dtype)
+    assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, "decode")
+
+
+def test_decode_split_count_invariance_and_zero_query_counts():
+    ctx = [1, 17, 1000, 4096, 2500]
+    case = decode_case(len(ctx), 32, 8, 128, ctx, 16, BF16, seeds=(21, 22, 23))
+    O_ref, L_ref = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                       case.ctx_lens, case.scale, BF16)
+    for split in (16, 64, 256, 1024, 4096, 8192):
+        say(f"decode split {split}")
+        O, LSE = run_decode(case, split)
+        assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, f"split {split}")
+        O0, L0 = run_decode(case, split, q_bits=np.zeros_like(case.q))
+        cnt = np.round(np.exp(L0.cpu().numpy().astype(np.float64)))
+        assert np.array_equal(cnt, np.repeat(case.ctx_lens[:, None].astype(float), 32, 1))
+
+
+def test_decode_block_table_logic_is_bit_exact():
+    ctx = [3, 16, 17, 999, 1024, 1025, 3333]
+    ident = decode_case(len(ctx), 16, 4, 128, ctx, 16, BF16, seeds=(31, 32, 33),
+                        identity_table=True)
+    shuf = permute_pages(ident, 4321)
+    O1, L1 = run_decode(ident, 256)
+    O2, L2 = run_decode(shuf, 256)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    O3, L3 = run_decode(ident, 256)                  # determinism
+    assert torch.equal(O1, O3) and torch.equal(L1, L3)
+
+
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+def test_decode_poisoned_slots_pages_and_guard_are_never_read(dtype):
+    ctx = [5, 16, 31, 1000, 77]
+    case = decode_case(len(ctx), 8, 2, 64, ctx, 16, dtype, seeds=(41, 42, 43),
+                       max_pages=80)
+    nan = NAN_BF16 if dtype == BF16 else NAN_F16
+    clean_O, clean_L = run_decode(case, 64)
+    # poison: a guard page in front of the pool, slots >= ctx in every last page, and two
+    # unreferenced pages at the end of the pool; unused table entries stay -1
+    P = case.num_pages
+    kp = np.full((P + 3, 16, case.Hkv, case.d), nan, np.uint16)
+    vp = np.full_like(kp, nan)
+    kp[1:P + 1] = case.k_pages
+    vp[1:P + 1] = case.v_pages
+    for r, n in enumerate(ctx):
+        last = case.block_table[r, (n - 1) // 16]
+        if n % 16:
+            kp[1 + last, n % 16:] = nan
+            vp[1 + last, n % 16:] = nan
+    O, L = run_decode(case, 64, k_pages=kp, v_pages=vp, pool_offset=1)
+    assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
+    assert torch.equal(O, clean_O) and torch.equal(L, clean_L)
+
+
+def test_decode_empty_context_and_no_lse():
+    case = decode_case(3, 8, 2, 128, [0, 40, 0], 16, BF16, seeds=(51, 52, 53), max_pages=4)
+    O, L = run_decode(case, 32)
+    o = O.float().cpu().numpy()
+    l = L.cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(o[2] == 0) and np.all(np.isneginf(l[[0, 2]]))
+    O_ref, L_ref = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                       case.ctx_lens, case.scale, BF16)
+    assert_parity(o[1], O_ref[1], l[1], L_ref[1], "ctx 40")
+    O2, _ = run_decode(case, 32, want_lse=False)
+    assert torch.equal(O, O2)
+
+
+def test_decode_named_workload_full_size_sampled_heads():
+    name = "paged_gqa_decode_b64_ctx512_32768"
+    c = CONFIGS[name]
+    say(f"decode full size {name}")
+    case = config_case(name)
+    O, LSE = run_decode(case, c["split_tokens"])
+    rng = np.random.default_rng(77)
+    pairs = []
+    long_r = int(np.argmax(case.ctx_lens))
+    short_r = int(np.argmin(case.ctx_lens))
+    for r in sorted({0, case.B - 1, long_r, short_r} | set(rng.integers(0, case.B, 8).tolist())):
+        for h in sorted({0, 3, 4, 31} | set(rng.integers(0, 32, 2).tolist())):
+            pairs.append(r * case.Hq + h)
+    pairs = np.array(pairs, np.int64)
+    O_ref, L_ref = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                       case.ctx_lens, case.scale, BF16, pairs=pairs)
+    idx = torch.from_numpy(pairs).cuda()
+    Og = from_dev_f64(O.view(-1, case.d)[idx])
+    Lg = LSE.view(-1)[idx].cpu().numpy()
+    assert_parity(Og, O_ref, Lg, L_ref, name)
+    assert torch.isfinite(O.float()).all() and torch.isfinite(LSE).all()
+    # zero-query count test at full size: exp(LSE) is the context length for every head
+    O0, L0 = run_decode(case, c["split_tokens"], q_bits=np.zeros_like(case.q))
+    cnt = np.round(np.exp(L0.cpu().numpy().astype(np.float64)))
+    assert np.array_equal(cnt, np.repeat(case.ctx_lens[:, None].astype(float), case.Hq, 1))
