@@ -24,7 +24,26 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is not built; run `python -m exact_attention_08_amd.build` "
         "(there is no non-HIP implementation to fall back to)")
 
+# One HIP runtime per process: torch brings its own libamdhip64 (same soname as ROCm's).
+# Loading torch first makes libattn.so's libamdhip64 dependency bind to that copy, so the
+# streams and device pointers torch hands over belong to the runtime that launches the
+# kernels.  Loading libattn.so first would pull in a second runtime.
+import torch  # noqa: E402,F401  (imported for its HIP runtime)
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:  # pragma: no cover
+        return []
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process "
+                      f"({_hip_runtimes_mapped()}); import torch before loading libattn.so")
 _P, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib.attn_fwd.argtypes = [_P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _f, _i, _P]
 _lib.attn_fwd.restype = _i

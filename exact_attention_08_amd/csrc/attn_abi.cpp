@@ -5,6 +5,8 @@
 // explicit error; LLM Internals 10.3.8 on silent fallback to the math path].
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/attn.h"
 #include "attn_internal.h"
@@ -14,6 +16,12 @@ namespace {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace
+
+hipError_t attn::report_launch(hipError_t e, const char* what) {
+    if (e != hipSuccess && getenv("ATTN_DEBUG"))
+        fprintf(stderr, "libattn: launching %s failed: %s\n", what, hipGetErrorString(e));
+    return e;
+}
 
 extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,

@@ -291,16 +291,14 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     float* ws_lse = (float*)((char*)a.workspace + (size_t)a.B * a.Hq * (size_t)S * D * sizeof(float));
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     hipStream_t st = (hipStream_t)a.stream;
-    hipLaunchKernelGGL((decode_split_kernel<D, IS_BF16>), dim3((unsigned)S, a.Hkv, a.B),
-                       dim3(kDecThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.Kpages,
-                       (const uint16_t*)a.Vpages, a.block_table, a.ctx_lens, ws_o, ws_lse, a.Hq,
-                       a.Hkv, a.max_pages, a.split_tokens, (int)S, scale_log2);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(decode_split_kernel<D, IS_BF16>, dim3((unsigned)S, a.Hkv, a.B),
+                                 dim3(kDecThreads), st, "decode_split_kernel", a.q, a.Kpages,
+                                 a.Vpages, a.block_table, a.ctx_lens, ws_o, ws_lse, a.Hq, a.Hkv,
+                                 a.max_pages, a.split_tokens, (int)S, scale_log2);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D, IS_BF16>), dim3((unsigned)(a.B * a.Hq)), dim3(D),
-                       0, st, ws_o, ws_lse, a.ctx_lens, (uint16_t*)a.O, a.LSE, a.Hq,
-                       a.split_tokens, (int)S);
-    return hipGetLastError();
+    return launch_kernel(decode_merge_kernel<D, IS_BF16>, dim3((unsigned)(a.B * a.Hq)), dim3(D),
+                         st, "decode_merge_kernel", ws_o, ws_lse, a.ctx_lens, a.O, a.LSE, a.Hq,
+                         a.split_tokens, (int)S);
 }
 
 }  // namespace

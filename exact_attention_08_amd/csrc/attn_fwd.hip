@@ -274,11 +274,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     const long long grid = n_group_items * G;
     const int remap = (n_group_items % 8 == 0) ? 1 : 0;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((prefill_fwd_kernel<D, IS_BF16, CAUSAL>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, (hipStream_t)a.stream,
-                       (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (uint16_t*)a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N, scale_log2, n_qtiles, remap);
-    return hipGetLastError();
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL>, dim3((unsigned)grid),
+                         dim3(kThreads), (hipStream_t)a.stream, "prefill_fwd_kernel", a.Q, a.K,
+                         a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N, scale_log2, n_qtiles, remap);
 }
 
 }  // namespace

@@ -34,6 +34,28 @@ struct DecodeArgs {
     void* stream;
 };
 
+// Launch through hipLaunchKernel so the status reflects this launch only (a sticky error
+// left by some earlier, unrelated HIP call must not be reported as ours).  With
+// ATTN_DEBUG set in the environment a failing launch prints the runtime's message.
+hipError_t report_launch(hipError_t e, const char* what);
+
+template <typename... KArgs>
+hipError_t launch_exact(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                        const char* what, KArgs... args) {
+    void* ptrs[] = {static_cast<void*>(&args)...};
+    return report_launch(hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs,
+                                         0, st),
+                         what);
+}
+
+// Converts every argument to the kernel's exact parameter type before taking its address.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                         const char* what, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    return launch_exact<KArgs...>(kern, grid, block, st, what, static_cast<KArgs>(args)...);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
