@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  1. attn_fwd on the GPT-2-medium-shaped causal prefill (B=64, H=16, N=1024, d=64, bf16);
+  2. attn_decode_paged on the paged GQA decode batch (64 sequences, Hq=32, Hkv=8, d=128,
+     16-token pages, log-uniform contexts in [512, 32768], 1024-token splits, bf16).
+Inputs are generated (seeded) and uploaded before the timed region.  W warm-up steps, then
+exactly K timed steps bracketed by torch.cuda.synchronize().  HIP events recorded on the
+stream the library launches on (torch's current stream) give each call's average duration.
+
+Printed: one JSON line.  `value` is the prefill throughput in TFLOP/s (algorithmic FLOPs:
+4*B*H*N^2*d/2 for causal); the decode half of the metric is in `decode` (algorithmic bytes:
+every K/V element of every context read once, plus q, O, block table and lengths).
+`roofline` covers the prefill kernel, `decode.roofline` the decode call; `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workloads.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--cpu-seconds 10] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+PREFILL = "gpt2_medium_b64_h16_n1024_d64_causal"
+DECODE = "paged_gqa_decode_b64_ctx512_32768"
+EXTRA = ["llama3_8b_prefill_n8192_causal", "llama3_8b_prefill_n32768_causal"]
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def prefill_flops(c):
+    f = 4.0 * c.B * c.Hq * c.N * c.N * c.d
+    return f * 0.5 if c.causal else f
+
+
+def prefill_bytes(c):
+    e = 2
+    return (2 * c.B * c.Hq * c.N * c.d * e          # Q read, O written
+            + 2 * c.B * c.Hkv * c.N * c.d * e       # K, V read
+            + c.B * c.Hq * c.N * 4)                 # LSE written
+
+
+def decode_bytes(c):
+    tokens = int(c.ctx_lens.astype("int64").sum())
+    pages = int(((c.ctx_lens.astype("int64") + c.page_size - 1) // c.page_size).sum())
+    kv = tokens * c.Hkv * c.d * 2 * 2               # K and V, bf16, each element once
+    qo = 2 * c.B * c.Hq * c.d * 2                   # q read, O written
+    meta = pages * 4 + c.B * 4 + c.B * c.Hq * 4     # block-table entries, lengths, LSE
+    return kv + qo + meta, kv
+
+
+def decode_flops(c):
+    return 4.0 * c.Hq * c.d * float(c.ctx_lens.astype("int64").sum())
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "exact_attention_08_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only if it was
+    taken on the current kernel source."""
+    path = os.path.join(TRAFFIC_DIR, f"{kernel_key}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def to_dev(bits, dtype):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == 0 else torch.float16).cuda()
+
+
+def cpu_baseline(pc, dc, seconds):
+    """The fp64 oracle on a bounded sample: random prefill rows, then random decode
+    (sequence, head) pairs, each leg running ~`seconds` of wall time on all host cores."""
+    import numpy as np
+    import oracle
+    threads = oracle.threads()
+    rng = np.random.default_rng(99)
+    # prefill leg: batches of rows until the time budget is used
+    rows_done, flops, t_pre = 0, 0.0, 0.0
+    while t_pre < seconds:
+        rows = rng.integers(0, pc.B * pc.Hq * pc.N, 8 * threads).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention(pc.q, pc.k, pc.v, pc.causal, pc.scale, pc.dtype, rows=rows)
+        t_pre += time.perf_counter() - t0
+        i = rows % pc.N
+        flops += float((4.0 * pc.d * ((i + 1) if pc.causal else np.full_like(i, pc.N))).sum())
+        rows_done += len(rows)
+    # decode leg
+    pairs_done, kv_bytes, t_dec = 0, 0.0, 0.0
+    while t_dec < seconds:
+        pairs = rng.integers(0, dc.B * dc.Hq, threads).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.decode_paged(dc.q, dc.k_pages, dc.v_pages, dc.block_table, dc.ctx_lens, dc.scale,
+                            dc.dtype, pairs=pairs)
+        t_dec += time.perf_counter() - t0
+        # per (sequence, head) the oracle reads that head's K/V rows once
+        kv_bytes += float((dc.ctx_lens[pairs // dc.Hq].astype(np.int64) * dc.d * 2 * 2).sum())
+        pairs_done += len(pairs)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {
+        "value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": (f"{rows_done} random query rows of the B64 H16 N1024 d64 causal prefill, "
+                   f"fp64, {t_pre:.1f} s"),
+        "cpu": model,
+        "decode": {"value": kv_bytes / t_dec / 1e9, "unit": "GB/s",
+                   "sample": (f"{pairs_done} random (sequence, head) pairs of the paged decode "
+                              f"batch, fp64, {t_dec:.1f} s; bytes = that head's K/V rows")},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the Llama-3-8B prefill figures")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="(profiling) run only one half of the step")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: this library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_08_amd as attn
+    from attn_inputs import CONFIGS, config_case
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
+
+    log("bench: generating inputs")
+    pc = config_case(PREFILL)
+    dc = config_case(DECODE)
+    split = CONFIGS[DECODE]["split_tokens"]
+    Q, K, V = (to_dev(x, pc.dtype) for x in (pc.q, pc.k, pc.v))
+    O = torch.empty_like(Q)
+    LSE = torch.empty(pc.B, pc.Hq, pc.N, dtype=torch.float32, device=dev)
+    q = to_dev(dc.q, dc.dtype)
+    kp, vp = to_dev(dc.k_pages, dc.dtype), to_dev(dc.v_pages, dc.dtype)
+    bt = torch.from_numpy(dc.block_table).to(dev)
+    ctx = torch.from_numpy(dc.ctx_lens).to(dev)
+    Od = torch.empty_like(q)
+    Ld = torch.empty(dc.B, dc.Hq, dtype=torch.float32, device=dev)
+    ws = torch.empty(attn.attn_decode_paged_workspace_bytes(dc.B, dc.Hq, dc.d, dc.page_size,
+                                                            dc.max_pages, split),
+                     dtype=torch.uint8, device=dev)
+    # a plain copy of known size, for calibrating HBM counters when profiled
+    cal = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+
+    do_pre = args.only in (None, "prefill")
+    do_dec = args.only in (None, "decode")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if do_pre:
+            attn.attn_fwd(Q, K, V, O, LSE, pc.causal, pc.scale)
+        if ev is not None:
+            ev[1].record()
+        if do_dec:
+            attn.attn_decode_paged(q, kp, vp, bt, ctx, Od, Ld, split, ws, dc.scale)
+        if ev is not None:
+            ev[2].record()
+
+    log(f"bench: {args.warmup} warm-up steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"bench: {args.steps} timed steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps * 1e-3   # seconds
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps * 1e-3
+    assert torch.isfinite(LSE).all() and torch.isfinite(Ld).all()
+
+    fl = prefill_flops(pc)
+    pb = prefill_bytes(pc)
+    db, kv_only = decode_bytes(dc)
+    pre_tflops = fl / t_pre / 1e12 if do_pre else None
+    dec_gbs = db / t_dec / 1e9 if do_dec else None
+    # the prefill's algorithmic intensity is below the ridge (8 TB/s x time > 2.5 PF x time),
+    # so its roofline is the HBM one
+    pre_bound_hbm = pb / (HBM_PEAK_GBS * 1e9) > fl / (MFMA_PEAK_TFLOPS * 1e12)
+    pre_digest = source_digest(["attn_fwd.hip", "attn_common.h"])
+    dec_digest = source_digest(["attn_decode.hip", "attn_common.h"])
+    pre_traffic = load_traffic("prefill_fwd_gpt2_medium", pre_digest)
+    dec_traffic = load_traffic("decode_paged_b64", dec_digest)
+
+    roof_pre = None
+    if do_pre:
+        if pre_bound_hbm:
+            ach = pb / t_pre / 1e9
+            roof_pre = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                        "traffic": pre_traffic, "kernel": "prefill_fwd_kernel<64,bf16,causal>",
+                        "algorithmic_bytes_per_launch": pb,
+                        "avg_launch_us": round(t_pre * 1e6, 2)}
+        else:
+            roof_pre = {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_PEAK_TFLOPS, 4),
+                        "traffic": pre_traffic, "kernel": "prefill_fwd_kernel<64,bf16,causal>",
+                        "avg_launch_us": round(t_pre * 1e6, 2)}
+    roof_dec = None
+    if do_dec:
+        roof_dec = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": dec_traffic,
+                    "kernel": "decode_split_kernel<128,bf16> + decode_merge_kernel<128,bf16>",
+                    "algorithmic_bytes_per_launch": db, "avg_launch_us": round(t_dec * 1e6, 2)}
+
+    extra = {}
+    if not args.no_extra and args.only is None:
+        for name in EXTRA:
+            log(f"bench: extra figure {name}")
+            c = config_case(name)
+            Qx, Kx, Vx = (to_dev(x, c.dtype) for x in (c.q, c.k, c.v))
+            Ox = torch.empty_like(Qx)
+            Lx = torch.empty(c.B, c.Hq, c.N, dtype=torch.float32, device=dev)
+            for _ in range(2):
+                attn.attn_fwd(Qx, Kx, Vx, Ox, Lx, c.causal, c.scale)
+            reps = 10 if c.N <= 8192 else 4
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                attn.attn_fwd(Qx, Kx, Vx, Ox, Lx, c.causal, c.scale)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps * 1e-3
+            tf = prefill_flops(c) / t / 1e12
+            extra[name] = {"tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                           "avg_launch_us": round(t * 1e6, 1)}
+            del Qx, Kx, Vx, Ox, Lx
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(pc, dc, args.cpu_seconds)
+
+    out = {
+        "metric": "prefill attn TFLOP/s (%MFMA peak); paged decode KV GB/s (%HBM peak)",
+        "value": round(pre_tflops, 2) if pre_tflops is not None else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded i.i.d. N(0,1), bf16)",
+        "config": {"workload": "gpt2-medium causal prefill B64 H16 N1024 d64 + paged GQA decode "
+                               "B64 Hq32 Hkv8 d128 ctx log-uniform[512,32768] page16 split1024",
+                   "prefill": {"B": pc.B, "H": pc.Hq, "N": pc.N, "d": pc.d, "causal": True},
+                   "decode": {"B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "d": dc.d,
+                              "page": dc.page_size, "split_tokens": split,
+                              "total_ctx_tokens": int(dc.ctx_lens.astype(np.int64).sum())},
+                   "parallelism": "single GPU"},
+        "mfma_frac": round(pre_tflops / MFMA_PEAK_TFLOPS, 4) if pre_tflops else None,
+        "roofline": roof_pre,
+        "decode": None if not do_dec else {
+            "value": round(dec_gbs, 1), "unit": "GB/s",
+            "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "kv_only_gbs": round(kv_only / t_dec / 1e9, 1),
+            "tflops": round(decode_flops(dc) / t_dec / 1e12, 2),
+            "roofline": roof_dec},
+        "extra_prefill": extra or None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
