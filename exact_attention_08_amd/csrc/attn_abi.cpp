@@ -17,6 +17,19 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
+int attn::device_cu_count() {
+    // per-device cache; a race between threads only repeats the same query
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
+
 hipError_t attn::report_launch(hipError_t e, const char* what) {
     if (e != hipSuccess && getenv("ATTN_DEBUG"))
         fprintf(stderr, "libattn: launching %s failed: %s\n", what, hipGetErrorString(e));

@@ -6,6 +6,7 @@
 //     rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
 //   v_mfma_f32_16x16x32_{bf16,f16}: A lane l holds row l%16, 8 k-values of k-group l/16;
 //     B lane l holds column l%16; D lane l holds column l%16 and rows 4*(l/16) + v, v = 0..3.
+//   v_mfma_f32_16x16x16_{bf16,f16}: as above with 4 k-values per lane (k-group l/16).
 // Only the pairing of A's and B's k-values matters for the product, so the kernels choose
 // the k order freely as long as A and B use the same one.
 #pragma once
@@ -19,6 +20,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -36,6 +39,10 @@ template <> struct Elem<true> {
     __device__ static inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                         __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
     }
     // two fp32 -> packed pair of 16-bit values (x in the low half)
     __device__ static inline uint32_t pack2(float x, float y) {
@@ -55,6 +62,10 @@ template <> struct Elem<false> {
     __device__ static inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
     }
     __device__ static inline uint32_t pack2(float x, float y) {
         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));

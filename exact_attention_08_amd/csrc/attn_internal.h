@@ -56,6 +56,9 @@ hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStrea
     return launch_exact<KArgs...>(kern, grid, block, st, what, static_cast<KArgs>(args)...);
 }
 
+// Compute units of the current device (queried once per device, then cached).
+int device_cu_count();
+
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
