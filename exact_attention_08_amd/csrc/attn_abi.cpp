@@ -44,6 +44,8 @@ extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, fl
     if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SHAPE;
     // element counts must stay addressable with 64-bit offsets and the grid in 32 bits
     if ((long long)B * Hq * (long long)N * d > (1LL << 46)) return ATTN_ERR_SHAPE;
+    // one head's rows are addressed with 32-bit byte offsets
+    if ((long long)N * d * 2 > (1LL << 30)) return ATTN_ERR_SHAPE;
     if ((long long)((N + 127) / 128) * B * Hq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;

@@ -74,8 +74,9 @@ enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
  *   probabilities feeding the second product are rounded to dtype (round-to-nearest-even),
  *   as is O.
  *
- *   Supported: d in {64, 128}; dtype bf16 or fp16; any N >= 1, B >= 1, Hq % Hkv == 0;
- *   scale finite and > 0.  All five pointers must be 16-byte aligned.
+ *   Supported: d in {64, 128}; dtype bf16 or fp16; N >= 1 with N * d * 2 <= 2^30 bytes per
+ *   head (N <= 4194304 at d = 128); B >= 1, Hq % Hkv == 0; scale finite and > 0.  All five
+ *   pointers must be 16-byte aligned.
  *   Returns ATTN_OK or a negative attn_status.
  */
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
