@@ -64,10 +64,17 @@ def decode_flops(c):
 
 
 def source_digest(files):
+    """Digest of the kernel sources with comments and whitespace removed, so that the
+    committed counter measurements stay valid across comment-only edits and are dropped
+    (traffic = null) as soon as the code changes."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "exact_attention_08_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "exact_attention_08_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,13 +1,13 @@
 // attn_fwd.hip -- fused exact attention forward (prefill) for gfx950.
 //
 // Method: FlashAttention-2 loop order [LLM Internals 10.3.2, tiled forward; 10.3.3]: one
-// workgroup owns a block of BR = 256 query rows of one (batch, head); the K_j/V_j column
-// blocks stream past it through LDS; for every block the running max m, the exp-sum l and
-// the unnormalised output O~ are updated, one division by l happens at the end, and only
-// O and LSE = m + ln l go back to HBM.  Fully masked causal blocks are never visited;
-// diagonal and ragged-tail blocks are masked element by element before the max
-// [zwjcode.cn FlashAttention blog, section 06; AI-infra handbook "FlashAttention and
-// inference operators", causal masking and the teaching kernel's kv_end bound].
+// workgroup owns a block of BR query rows of one (batch, head); the K_j/V_j column blocks
+// stream past it through LDS; for every block the running max m, the exp-sum l and the
+// unnormalised output O~ are updated, one division by l happens at the end, and only O and
+// LSE = m + ln l go back to HBM.  Fully masked causal blocks are never visited; diagonal
+// and ragged-tail blocks are masked element by element before the max [zwjcode.cn
+// FlashAttention blog, section 06; AI-infra handbook "FlashAttention and inference
+// operators", causal masking and the teaching kernel's kv_end bound].
 //
 // Rescaling follows FlashAttention-4's conditional rescale [CS349D Lecture 4 notes, 3.5]
 // in an exact form: the exponentials are taken relative to a reference max m_ref, which is
@@ -17,17 +17,17 @@
 // are the same quantities as with the per-block rescale.
 //
 // MI355X mapping (not the pages' CUDA design):
-//   * 4 waves x 64 query rows (two 32-row column blocks per wave).  Each wave computes
+//   * 4 waves per workgroup, two waves per SIMD.  A wave owns QB column blocks of 32 query
+//     rows (QB = 1 at d = 128, 2 at d = 64; BR = 128 * QB).  It computes
 //     S^T = K_j Q_i^T with v_mfma_f32_32x32x16: keys are the MFMA rows and queries its
 //     columns, so one lane holds 16 scores of ONE query row per 32-key block.  Row max /
 //     row sum are in-lane reductions plus one exchange with the lane 32 away; the
 //     exponentiated scores, rounded to 16 bits, are already the B operand of
 //     O^T = V_j^T P^T, so P never leaves registers, and the rescale factor is a per-lane
-//     scalar.  Every K or V operand read from LDS feeds both column blocks, so LDS traffic
-//     is 1/64 byte per flop (the LDS port, not the matrix core, bounds a 32-row wave).
-//     At d = 128 a wave holds ~370 registers (accumulators in AGPRs): one wave per SIMD,
-//     whose two column blocks keep the matrix core busy while the other block's softmax
-//     runs on the VALU.
+//     scalar.  With two column blocks every K or V operand read from LDS feeds two
+//     products.
+//   * A KV tile is processed as 32-key blocks; the next block's K operands and the current
+//     block's V operands are read from LDS ahead of their use.
 //   * Q stays in registers for the whole KV sweep (B operand of the first product).
 //   * K_j is staged row-major in LDS, V_j transposed (d-major) with the key order inside
 //     each 16-key chunk permuted so every MFMA operand is one 16-byte LDS read; rows are
