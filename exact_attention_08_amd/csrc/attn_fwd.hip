@@ -49,10 +49,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;     // log2 headroom before the reference max moves
 
 // Per head size: BC keys per KV tile, QB 32-row query blocks per wave (BR = 128 * QB rows
-// per workgroup), two waves per SIMD.
+// per workgroup), OCC waves per SIMD (the register budget is 512 / OCC per wave).
 template <int D> struct PrefillTile;
-template <> struct PrefillTile<128> { static constexpr int BC = 64, QB = 1; };
-template <> struct PrefillTile<64> { static constexpr int BC = 128, QB = 2; };
+template <> struct PrefillTile<128> { static constexpr int BC = 64, QB = 1, OCC = 2; };
+template <> struct PrefillTile<64> { static constexpr int BC = 64, QB = 1, OCC = 2; };
 
 struct WorkItem { int qt, b, h, kvh; };
 
@@ -85,7 +85,7 @@ __device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int byt
 }
 
 template <int D, bool IS_BF16, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(
+__global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int B, int Hq, int Hkv, int N, float scale_log2, int n_qtiles, int xcd_major) {
@@ -97,12 +97,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(
     constexpr int NKS = D / 16;          // k-steps of the first product
     constexpr int NDB = D / 32;          // 32-wide d blocks of the output
     constexpr int KSTR = D + 8;          // LDS row stride of K (elements)
-    constexpr int VSTR = BC + 8;         // LDS row stride of V^T (elements)
+    constexpr int VSTR = D + 32;         // LDS row stride of V (elements)
     constexpr int KCH = D / 8;           // 16-byte chunks per K/V row
     constexpr int KLOADS = BC * KCH / kThreads;   // K chunks per thread
-    constexpr int STAGE = BC * KSTR + D * VSTR;   // elements per LDS stage
-    static_assert(KLOADS * kThreads == BC * KCH, "K tile must split evenly");
-    static_assert((BC / 4) * KCH == kThreads, "one V unit (4 keys x 8 dims) per thread");
+    constexpr int STAGE = BC * (KSTR + VSTR);     // elements per LDS stage
+    static_assert(KLOADS * kThreads == BC * KCH, "K/V tile must split evenly");
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
@@ -141,12 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(
                 rq, ((q0w + 32 * qb + l32) * D + ks * 16 + g * 8) * 2, 0, 0);
 
     // a3: register staging of one K/V tile
-    u32x4 kreg[KLOADS], vreg[4];
-    const int v_kg = tid % (BC / 4);          // 4-key group of this thread's V unit
-    const int v_dc = tid / (BC / 4);          // 8-dim chunk of this thread's V unit
-    // transposed position of the 4-key group: swap bits 0 and 1 of the group index so that
-    // MFMA k-values (8g + e) of a 16-key chunk are contiguous in LDS
-    const int v_kgp = (v_kg & ~3) | ((v_kg & 1) << 1) | ((v_kg >> 1) & 1);
+    u32x4 kreg[KLOADS], vreg[KLOADS];
 
     auto load_tile = [&](int j) {
         const int key0 = j * BC;
@@ -157,26 +151,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(
             kreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((key0 + row) * D + col) * 2, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            vreg[e] = __builtin_amdgcn_raw_buffer_load_b128(
-                rv, ((key0 + v_kg * 4 + e) * D + v_dc * 8) * 2, 0, 0);
+        for (int r = 0; r < KLOADS; ++r) {
+            const int c = tid + r * kThreads;
+            const int row = c / KCH, col = (c % KCH) * 8;
+            vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((key0 + row) * D + col) * 2, 0, 0);
+        }
     };
     auto store_tile = [&](int stage) {
         uint16_t* Ks = lds + stage * STAGE;
-        uint16_t* Vt = Ks + BC * KSTR;
+        uint16_t* Vs = Ks + BC * KSTR;
 #pragma unroll
         for (int r = 0; r < KLOADS; ++r) {
             const int c = tid + r * kThreads;
             const int row = c / KCH, col = (c % KCH) * 8;
             *reinterpret_cast<u32x4*>(&Ks[row * KSTR + col]) = kreg[r];
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int d = v_dc * 8 + 2 * p;
-            *reinterpret_cast<u32x2*>(&Vt[d * VSTR + v_kgp * 4]) =
-                pack_col_lo(vreg[0][p], vreg[1][p], vreg[2][p], vreg[3][p]);
-            *reinterpret_cast<u32x2*>(&Vt[(d + 1) * VSTR + v_kgp * 4]) =
-                pack_col_hi(vreg[0][p], vreg[1][p], vreg[2][p], vreg[3][p]);
+            *reinterpret_cast<u32x4*>(&Vs[row * VSTR + col]) = vreg[r];
         }
     };
 
@@ -192,63 +181,99 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(
         for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
     }
 
-    // One KV tile for this wave, as 32-key blocks: K operands are read once and feed the
-    // S^T products of both column blocks; V operands likewise feed both O^T updates.
-    // `diag` (wave-uniform): the tile crosses the causal diagonal of this wave's rows, so
-    // scores of keys after the query row are masked; keys past N are masked in the ragged
-    // last block.  A fully masked row block yields zero weights.
-    auto compute_tile = [&](const uint16_t* Ks, const uint16_t* Vt, int key0, bool diag) {
-        auto read_k = [&](u32x4 (&ka)[NKS], int kb) {
+    // The KV sweep runs as a software pipeline over 32-key blocks.  Iteration b:
+    //   1. read block b's V operands; read the next block's K operands (same tile);
+    //   2. statistics of block b's scores (mask, max, the rare rescale) -- branches here;
+    //   3. at the last block of a tile: store the next tile (already in registers) into
+    //      the other LDS stage, barrier, start fetching the tile after it from HBM, and read
+    //      the next block's K operands from the new stage;
+    //   4. one branch-free region: the next block's S^T MFMAs, block b's exponentials,
+    //      sums and packing, and block b's O^T MFMAs -- independent matrix and vector work
+    //      the scheduler interleaves, so the softmax runs under the matrix cores.
+    // Blocks whose first key lies after the wave's last row (causal) are skipped by the
+    // wave; it still takes part in the tile stores and barriers.  Near the end the "next"
+    // S^T is computed on the current block and discarded, keeping step 4 branch free.
+    const int nb = n_kv * NKB;
+    const int nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, wave_last_q / 32 + 1) : nb);
+
+    // V^T operand of the second product from row-major V with the transposing LDS read
+    // (ds_read_b64_tr_b16): within each 16-lane group G, destination lane i receives, as
+    // element e, the (i % 4)-th 16-bit value of the 8 bytes addressed by lane 16G + 4e + i/4.
+    // Lane 16G + 4e + a therefore addresses key 4(G >> 1) + e, dims 16(G & 1) + 4a..+3 of the
+    // 16-key step, and lane l = 16G + i receives dim 16(G & 1) + i (= l % 32) for keys
+    // 4(G >> 1) + 0..3; a second read 8 keys further gives keys 8 + 4(G >> 1) + 0..3.  These
+    // are exactly the keys, in the same order, that the lane's P operand holds.
+    const int v_lane = (4 * ((lane >> 5) & 1) + ((lane >> 2) & 3)) * VSTR + 16 * ((lane >> 4) & 1) +
+                       4 * (lane & 3);
+    auto read_tr = [&](const uint16_t* p) -> u32x2 {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p));
+        return __builtin_bit_cast(u32x2, v);
+    };
+    auto read_k = [&](u32x4 (&ka)[NKS], const uint16_t* Ks, int kb) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                ka[ks] = *reinterpret_cast<const u32x4*>(&Ks[(kb * 32 + l32) * KSTR + ks * 16 + g * 8]);
-        };
-        // LDS operands are read one step ahead of their use: the next block's K operands
-        // while this block's softmax runs, this block's V operands before its S^T product.
-        u32x4 ka[2][NKS];
-        read_k(ka[0], 0);
+        for (int ks = 0; ks < NKS; ++ks)
+            ka[ks] = *reinterpret_cast<const u32x4*>(&Ks[(kb * 32 + l32) * KSTR + ks * 16 + g * 8]);
+    };
+    auto s_product = [&](const u32x4 (&ka)[NKS], f32x16 (&sacc)[kQB]) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const int kfirst = key0 + kb * 32;
-            u32x4 va[2][NDB];
+        for (int qb = 0; qb < kQB; ++qb) {
+            sacc[qb] = E::mfma32(ka[0], qreg[qb][0], f32x16{});
+#pragma unroll
+            for (int ks = 1; ks < NKS; ++ks) sacc[qb] = E::mfma32(ka[ks], qreg[qb][ks], sacc[qb]);
+        }
+    };
+
+    // One 32-key block.  sc holds this block's S^T, sn receives the next block's; the two
+    // are distinct registers (the caller alternates them), so the next block's MFMAs carry
+    // no register dependence on this block's exponentials and can overlap them.
+    auto block = [&](int j, int kb, f32x16 (&sc)[kQB], f32x16 (&sn)[kQB]) {
+        const uint16_t* Ks = lds + (j & 1) * STAGE;
+        const uint16_t* Vs = Ks + BC * KSTR;
+        const uint16_t* Ks_next = lds + ((j + 1) & 1) * STAGE;
+        const int bi = j * NKB + kb;
+        const int kfirst = bi * 32;
+        const bool live = bi < nb_live;            // wave-uniform
+        u32x4 va[2][NDB];
+        u32x4 ka[NKS];
+        float m_use[kQB];
+        if (live) {
+            // 1. operands
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    va[h][db] = *reinterpret_cast<const u32x4*>(
-                        &Vt[(db * 32 + l32) * VSTR + (2 * kb + h) * 16 + g * 8]);
-            // a4: S^T per column block
-            f32x16 sacc[kQB];
+                for (int db = 0; db < NDB; ++db) {
+                    const uint16_t* vp = Vs + v_lane + (kb * 32 + 16 * h) * VSTR + db * 32;
+                    const u32x2 lo = read_tr(vp);
+                    const u32x2 hi = read_tr(vp + 8 * VSTR);
+                    va[h][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+            if (kb + 1 < NKB) read_k(ka, Ks, kb + 1);
+            // 2. statistics
+            const bool mask_blk = (CAUSAL && kfirst + 31 > q0w) || kfirst + 32 > N;
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) {
-                sacc[qb] = E::mfma32(ka[kb & 1][0], qreg[qb][0], f32x16{});
-#pragma unroll
-                for (int ks = 1; ks < NKS; ++ks)
-                    sacc[qb] = E::mfma32(ka[kb & 1][ks], qreg[qb][ks], sacc[qb]);
-            }
-            if (kb + 1 < NKB) read_k(ka[(kb + 1) & 1], kb + 1);
-            const bool mask_blk = diag || kfirst + 32 > N;   // wave-uniform
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                const int q = q0w + 32 * qb + l32;
-                f32x16 sv = sacc[qb];
                 // a5: elementwise mask (select, never multiply)
                 if (mask_blk) {
+                    const int q = q0w + 32 * qb + l32;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int key = kfirst + 8 * (v >> 2) + 4 * g + (v & 3);
                         const bool masked = key >= N || (CAUSAL && key > q);
-                        sv[v] = masked ? -INFINITY : sv[v];
+                        sc[qb][v] = masked ? -INFINITY : sc[qb][v];
                     }
                 }
-                // a6: online softmax statistics, base 2, relative to the reference max
-                float mloc = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+                // a6: this lane sees half of the block's keys for its row; the half
+                // maximum decides whether the reference may stay.  Only when some lane's
+                // half exceeds it are the two halves combined (lanes l and l^32 hold the
+                // same row), so both halves always agree on m_ref.
+                float mloc = fmaxf(fmaxf(sc[qb][0], sc[qb][1]), sc[qb][2]);
 #pragma unroll
-                for (int v = 3; v < 16; ++v) mloc = fmaxf(mloc, sv[v]);
-                mloc = fmaxf(mloc, xor_lanes(mloc, 32));
-                const float m_blk = mloc * scale_log2;
-                const bool move = m_blk > m_ref[qb] + kRescaleSlack;
-                if (__ballot(move)) {
+                for (int v = 3; v < 16; ++v) mloc = fmaxf(mloc, sc[qb][v]);
+                if (__ballot(mloc * scale_log2 > m_ref[qb] + kRescaleSlack)) {
+                    const float m_blk = fmaxf(mloc, xor_lanes(mloc, 32)) * scale_log2;
+                    const bool move = m_blk > m_ref[qb] + kRescaleSlack;
                     const float m_new = move ? m_blk : m_ref[qb];
                     const float alpha = fast_exp2(m_ref[qb] - m_new);   // 0 on the first block
                     l_run[qb] *= alpha;
@@ -256,11 +281,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(
                     for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
                     m_ref[qb] = m_new;
                 }
-                const float m_use = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
+                m_use[qb] = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
+            }
+        }
+        // 3. tile boundary
+        if (kb == NKB - 1) {
+            if (j + 1 < n_kv) store_tile((j + 1) & 1);
+            __syncthreads();
+            if (j + 2 < n_kv) load_tile(j + 2);
+            if (live) read_k(ka, Ks_next, 0);
+        }
+        // 4. next S^T, this block's weights and O^T update
+        if (live) {
+            s_product(ka, sn);
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) {
                 float p[16];
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    p[v] = fast_exp2(__builtin_fmaf(sv[v], scale_log2, -m_use));
+                    p[v] = fast_exp2(__builtin_fmaf(sc[qb][v], scale_log2, -m_use[qb]));
                 float lsum = 0.f;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) lsum += p[v];
@@ -273,27 +312,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(
                                       E::pack2(p[8 * h + 4], p[8 * h + 5]),
                                       E::pack2(p[8 * h + 6], p[8 * h + 7])};
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) oacc[qb][db] = E::mfma32(va[h][db], pk, oacc[qb][db]);
+                    for (int db = 0; db < NDB; ++db)
+                        oacc[qb][db] = E::mfma32(va[h][db], pk, oacc[qb][db]);
                 }
             }
         }
     };
 
-    // KV sweep: tile j computes from LDS stage j&1 while tile j+1 is written to the other
-    // stage and tile j+2 is in flight from HBM; one barrier per tile.
     load_tile(0);
     store_tile(0);
     __syncthreads();
     if (n_kv > 1) load_tile(1);
+
+    static_assert(NKB == 2, "the block loop alternates two score buffers over two blocks per tile");
+    f32x16 s_a[kQB], s_b[kQB];
+    if (nb_live > 0) {
+        u32x4 ka[NKS];
+        read_k(ka, lds, 0);
+        s_product(ka, s_a);
+    }
     for (int j = 0; j < n_kv; ++j) {
-        const uint16_t* Ks = lds + (j & 1) * STAGE;
-        const uint16_t* Vt = Ks + BC * KSTR;
-        const int key0 = j * BC;
-        if (wave_live && !(CAUSAL && key0 > wave_last_q))
-            compute_tile(Ks, Vt, key0, CAUSAL && key0 + BC - 1 > q0w);
-        if (j + 1 < n_kv) store_tile((j + 1) & 1);
-        __syncthreads();
-        if (j + 2 < n_kv) load_tile(j + 2);
+        block(j, 0, s_a, s_b);
+        block(j, 1, s_b, s_a);
     }
 
     // a8: epilogue -- O = O~ / l, LSE = (m_ref + log2 l) ln 2
