@@ -52,14 +52,15 @@ constexpr float kRescaleSlack = 8.0f;     // log2 headroom before the reference 
 // per workgroup), OCC waves per SIMD (the register budget is 512 / OCC per wave).
 template <int D> struct PrefillTile;
 template <> struct PrefillTile<128> { static constexpr int BC = 64, QB = 1, OCC = 2; };
-template <> struct PrefillTile<64> { static constexpr int BC = 64, QB = 1, OCC = 2; };
+template <> struct PrefillTile<64> { static constexpr int BC = 64, QB = 1, OCC = 3; };
 
 struct WorkItem { int qt, b, h, kvh; };
 
-// a1: hardware workgroup id -> (q tile, batch, head).  A head group is a (batch, kv head)
-// with its G query heads; its n_qtiles * G items are numbered heaviest tile first.  When
-// the head groups divide evenly over the 8 XCDs (workgroups reach XCDs round robin), head
-// group hg runs entirely on XCD hg % 8, so its K/V stays in that XCD's L2.
+// a1: work item -> (q tile, batch, head).  A head group is a (batch, kv head) with its G
+// query heads; its n_qtiles * G items are numbered heaviest tile first.  When the head
+// groups divide evenly over the 8 XCDs (workgroups reach XCDs round robin), items are
+// interleaved so that item i belongs to XCD i % 8 and head group hg lives entirely on XCD
+// hg % 8, so its K/V stays in that XCD's L2.
 __device__ inline WorkItem prefill_work_item(int bid, int n_qtiles, int Hkv, int G,
                                              int xcd_major) {
     const int per = n_qtiles * G;
@@ -84,11 +85,11 @@ __device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int byt
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
-template <int D, bool IS_BF16, bool CAUSAL>
+template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST>
 __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int B, int Hq, int Hkv, int N, float scale_log2, int n_qtiles, int xcd_major) {
+    int B, int Hq, int Hkv, int N, float scale_log2, int n_qtiles, int n_items, int xcd_major) {
     using E = Elem<IS_BF16>;
     constexpr int BC = PrefillTile<D>::BC;
     constexpr int kQB = PrefillTile<D>::QB;
@@ -105,255 +106,276 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int g = lane >> 5;
     const int G = Hq / Hkv;
 
-    const WorkItem wi = prefill_work_item(blockIdx.x, n_qtiles, Hkv, G, xcd_major);
-    const int64_t qh_off = ((int64_t)wi.b * Hq + wi.h) * (int64_t)N;      // row offset of (b,h)
-    const int64_t kh_off = ((int64_t)wi.b * Hkv + wi.kvh) * (int64_t)N;   // row offset of (b,kvh)
-    const int head_bytes = N * D * 2;
-    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + qh_off * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + kh_off * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + kh_off * D, head_bytes);
+    // Items per workgroup.  Without PERSIST there is one workgroup per item, this loop runs
+    // once and the hardware dispatcher hands out the items.  With a smaller, persistent grid
+    // (short items, where the gap between one workgroup ending and the next starting on a CU
+    // costs more than the spread in workgroup speeds), workgroup b stays on XCD b % P
+    // (P = 8 when items are XCD-interleaved, else 1; workgroups reach the XCDs round robin)
+    // and takes that XCD's items in rounds of W, the workgroups of that XCD: forward on even
+    // rounds and backward on odd ones, so heavy and light causal tiles pair up.
+    const int P = xcd_major ? 8 : 1;
+    const int x = blockIdx.x % P, w = blockIdx.x / P;
+    const int W = ((int)gridDim.x - x + P - 1) / P;
+    const int n_slots = (n_items - x + P - 1) / P;
+    for (int round = 0;; ++round) {
+        const int slot = round * W + ((round & 1) ? W - 1 - w : w);
+        if (slot >= n_slots) break;
+        // the previous item's last LDS reads must be done before this item's first store
+        if (round > 0) __syncthreads();
+        // Lane indices are rederived per item (the empty asm hides that they are loop
+        // invariant): kept live across the item loop they would cost registers.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l32 = lane & 31;
+        const int g = lane >> 5;
+        const WorkItem wi = prefill_work_item(slot * P + x, n_qtiles, Hkv, G, xcd_major);
+        const int64_t qh_off = ((int64_t)wi.b * Hq + wi.h) * (int64_t)N;      // row offset of (b,h)
+        const int64_t kh_off = ((int64_t)wi.b * Hkv + wi.kvh) * (int64_t)N;   // row offset of (b,kvh)
+        const int head_bytes = N * D * 2;
+        const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + qh_off * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + kh_off * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + kh_off * D, head_bytes);
 
-    const int q_tile0 = wi.qt * kBR;
-    const int q0w = q_tile0 + wave * (32 * kQB);   // first query row of this wave
-    const bool wave_live = q0w < N;
+        const int q_tile0 = wi.qt * kBR;
+        const int q0w = q_tile0 + wave * (32 * kQB);   // first query row of this wave
+        const bool wave_live = q0w < N;
 
-    // KV tiles this workgroup visits: causal stops after the block holding its last row.
-    const int kv_last = CAUSAL ? min(N, q_tile0 + kBR) - 1 : N - 1;
-    const int n_kv = kv_last / BC + 1;
-    const int wave_last_q = min(q0w + 32 * kQB - 1, N - 1);
+        // KV tiles this workgroup visits: causal stops after the block holding its last row.
+        const int kv_last = CAUSAL ? min(N, q_tile0 + kBR) - 1 : N - 1;
+        const int n_kv = kv_last / BC + 1;
+        const int wave_last_q = min(q0w + 32 * kQB - 1, N - 1);
 
-    // a2: this lane's Q rows (one per column block) as the B operand of S^T = K Q^T
-    // (k-values d = 16ks + 8g..+7); rows past N read as zero
-    u32x4 qreg[kQB][NKS];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            qreg[qb][ks] = __builtin_amdgcn_raw_buffer_load_b128(
-                rq, ((q0w + 32 * qb + l32) * D + ks * 16 + g * 8) * 2, 0, 0);
+        // a2: this lane's Q rows (one per column block) as the B operand of S^T = K Q^T
+        // (k-values d = 16ks + 8g..+7); rows past N read as zero
+        u32x4 qreg[kQB][NKS];
+    #pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+    #pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                qreg[qb][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rq, ((q0w + 32 * qb + l32) * D + ks * 16 + g * 8) * 2, 0, 0);
 
-    // a3: register staging of one K/V tile
-    u32x4 kreg[KLOADS], vreg[KLOADS];
+        // a3: register staging of one K/V tile
+        u32x4 kreg[KLOADS], vreg[KLOADS];
 
-    auto load_tile = [&](int j) {
-        const int key0 = j * BC;
-#pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int c = tid + r * kThreads;
-            const int row = c / KCH, col = (c % KCH) * 8;
-            kreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((key0 + row) * D + col) * 2, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int c = tid + r * kThreads;
-            const int row = c / KCH, col = (c % KCH) * 8;
-            vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((key0 + row) * D + col) * 2, 0, 0);
-        }
-    };
-    auto store_tile = [&](int stage) {
-        uint16_t* Ks = lds + stage * STAGE;
-        uint16_t* Vs = Ks + BC * KSTR;
-#pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int c = tid + r * kThreads;
-            const int row = c / KCH, col = (c % KCH) * 8;
-            *reinterpret_cast<u32x4*>(&Ks[row * KSTR + col]) = kreg[r];
-            *reinterpret_cast<u32x4*>(&Vs[row * VSTR + col]) = vreg[r];
-        }
-    };
+        auto load_tile = [&](int j) {
+            const int key0 = j * BC;
+    #pragma unroll
+            for (int r = 0; r < KLOADS; ++r) {
+                const int c = tid + r * kThreads;
+                const int row = c / KCH, col = (c % KCH) * 8;
+                kreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((key0 + row) * D + col) * 2, 0, 0);
+            }
+    #pragma unroll
+            for (int r = 0; r < KLOADS; ++r) {
+                const int c = tid + r * kThreads;
+                const int row = c / KCH, col = (c % KCH) * 8;
+                vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((key0 + row) * D + col) * 2, 0, 0);
+            }
+        };
+        auto store_tile = [&](int stage) {
+            uint16_t* Ks = lds + stage * STAGE;
+            uint16_t* Vs = Ks + BC * KSTR;
+    #pragma unroll
+            for (int r = 0; r < KLOADS; ++r) {
+                const int c = tid + r * kThreads;
+                const int row = c / KCH, col = (c % KCH) * 8;
+                *reinterpret_cast<u32x4*>(&Ks[row * KSTR + col]) = kreg[r];
+                *reinterpret_cast<u32x4*>(&Vs[row * VSTR + col]) = vreg[r];
+            }
+        };
 
-    // a6 state, per column block (fp32, per lane = per query row; l is this lane's half
-    // of the keys)
-    float m_ref[kQB], l_run[kQB];
-    f32x16 oacc[kQB][NDB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        m_ref[qb] = -INFINITY;
-        l_run[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
-    }
-
-    // The KV sweep runs as a software pipeline over 32-key blocks.  Iteration b:
-    //   1. read block b's V operands; read the next block's K operands (same tile);
-    //   2. statistics of block b's scores (mask, max, the rare rescale) -- branches here;
-    //   3. at the last block of a tile: store the next tile (already in registers) into
-    //      the other LDS stage, barrier, start fetching the tile after it from HBM, and read
-    //      the next block's K operands from the new stage;
-    //   4. one branch-free region: the next block's S^T MFMAs, block b's exponentials,
-    //      sums and packing, and block b's O^T MFMAs -- independent matrix and vector work
-    //      the scheduler interleaves, so the softmax runs under the matrix cores.
-    // Blocks whose first key lies after the wave's last row (causal) are skipped by the
-    // wave; it still takes part in the tile stores and barriers.  Near the end the "next"
-    // S^T is computed on the current block and discarded, keeping step 4 branch free.
-    const int nb = n_kv * NKB;
-    const int nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, wave_last_q / 32 + 1) : nb);
-
-    // V^T operand of the second product from row-major V with the transposing LDS read
-    // (ds_read_b64_tr_b16): within each 16-lane group G, destination lane i receives, as
-    // element e, the (i % 4)-th 16-bit value of the 8 bytes addressed by lane 16G + 4e + i/4.
-    // Lane 16G + 4e + a therefore addresses key 4(G >> 1) + e, dims 16(G & 1) + 4a..+3 of the
-    // 16-key step, and lane l = 16G + i receives dim 16(G & 1) + i (= l % 32) for keys
-    // 4(G >> 1) + 0..3; a second read 8 keys further gives keys 8 + 4(G >> 1) + 0..3.  These
-    // are exactly the keys, in the same order, that the lane's P operand holds.
-    const int v_lane = (4 * ((lane >> 5) & 1) + ((lane >> 2) & 3)) * VSTR + 16 * ((lane >> 4) & 1) +
-                       4 * (lane & 3);
-    auto read_tr = [&](const uint16_t* p) -> u32x2 {
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(p));
-        return __builtin_bit_cast(u32x2, v);
-    };
-    auto read_k = [&](u32x4 (&ka)[NKS], const uint16_t* Ks, int kb) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            ka[ks] = *reinterpret_cast<const u32x4*>(&Ks[(kb * 32 + l32) * KSTR + ks * 16 + g * 8]);
-    };
-    auto s_product = [&](const u32x4 (&ka)[NKS], f32x16 (&sacc)[kQB]) {
-#pragma unroll
+        // a6 state, per column block (fp32, per lane = per query row; l is this lane's half
+        // of the keys)
+        float m_ref[kQB], l_run[kQB];
+        f32x16 oacc[kQB][NDB];
+    #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
-            sacc[qb] = E::mfma32(ka[0], qreg[qb][0], f32x16{});
-#pragma unroll
-            for (int ks = 1; ks < NKS; ++ks) sacc[qb] = E::mfma32(ka[ks], qreg[qb][ks], sacc[qb]);
+            m_ref[qb] = -INFINITY;
+            l_run[qb] = 0.f;
+    #pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
         }
-    };
 
-    // One 32-key block.  sc holds this block's S^T, sn receives the next block's; the two
-    // are distinct registers (the caller alternates them), so the next block's MFMAs carry
-    // no register dependence on this block's exponentials and can overlap them.
-    auto block = [&](int j, int kb, f32x16 (&sc)[kQB], f32x16 (&sn)[kQB]) {
-        const uint16_t* Ks = lds + (j & 1) * STAGE;
-        const uint16_t* Vs = Ks + BC * KSTR;
-        const uint16_t* Ks_next = lds + ((j + 1) & 1) * STAGE;
-        const int bi = j * NKB + kb;
-        const int kfirst = bi * 32;
-        const bool live = bi < nb_live;            // wave-uniform
-        u32x4 va[2][NDB];
-        u32x4 ka[NKS];
-        float m_use[kQB];
-        if (live) {
-            // 1. operands
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const uint16_t* vp = Vs + v_lane + (kb * 32 + 16 * h) * VSTR + db * 32;
-                    const u32x2 lo = read_tr(vp);
-                    const u32x2 hi = read_tr(vp + 8 * VSTR);
-                    va[h][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                }
-            if (kb + 1 < NKB) read_k(ka, Ks, kb + 1);
-            // 2. statistics
-            const bool mask_blk = (CAUSAL && kfirst + 31 > q0w) || kfirst + 32 > N;
-#pragma unroll
+        // The KV sweep runs as a software pipeline over 32-key blocks.  Iteration b:
+        //   1. read block b's V operands; read the next block's K operands (same tile);
+        //   2. statistics of block b's scores (mask, max, the rare rescale) -- branches here;
+        //   3. at the last block of a tile: store the next tile (already in registers) into
+        //      the other LDS stage, barrier, start fetching the tile after it from HBM, and read
+        //      the next block's K operands from the new stage;
+        //   4. one branch-free region: the next block's S^T MFMAs, block b's exponentials,
+        //      sums and packing, and block b's O^T MFMAs -- independent matrix and vector work
+        //      the scheduler interleaves, so the softmax runs under the matrix cores.
+        // Blocks whose first key lies after the wave's last row (causal) are skipped by the
+        // wave; it still takes part in the tile stores and barriers.  Near the end the "next"
+        // S^T is computed on the current block and discarded, keeping step 4 branch free.
+        const int nb = n_kv * NKB;
+        const int nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, wave_last_q / 32 + 1) : nb);
+
+        // V^T operand of the second product from row-major V with the transposing LDS read
+        // (ds_read_b64_tr_b16): within each 16-lane group G, destination lane i receives, as
+        // element e, the (i % 4)-th 16-bit value of the 8 bytes addressed by lane 16G + 4e + i/4.
+        // Lane 16G + 4e + a therefore addresses key 4(G >> 1) + e, dims 16(G & 1) + 4a..+3 of the
+        // 16-key step, and lane l = 16G + i receives dim 16(G & 1) + i (= l % 32) for keys
+        // 4(G >> 1) + 0..3; a second read 8 keys further gives keys 8 + 4(G >> 1) + 0..3.  These
+        // are exactly the keys, in the same order, that the lane's P operand holds.
+        const int v_lane = (4 * ((lane >> 5) & 1) + ((lane >> 2) & 3)) * VSTR + 16 * ((lane >> 4) & 1) +
+                           4 * (lane & 3);
+        auto read_tr = [&](const uint16_t* p) -> u32x2 {
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(p));
+            return __builtin_bit_cast(u32x2, v);
+        };
+        auto read_k = [&](u32x4 (&ka)[NKS], const uint16_t* Ks, int kb) {
+    #pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                ka[ks] = *reinterpret_cast<const u32x4*>(&Ks[(kb * 32 + l32) * KSTR + ks * 16 + g * 8]);
+        };
+        auto s_product = [&](const u32x4 (&ka)[NKS], f32x16 (&sacc)[kQB]) {
+    #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) {
-                // a5: elementwise mask (select, never multiply)
-                if (mask_blk) {
-                    const int q = q0w + 32 * qb + l32;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = kfirst + 8 * (v >> 2) + 4 * g + (v & 3);
-                        const bool masked = key >= N || (CAUSAL && key > q);
-                        sc[qb][v] = masked ? -INFINITY : sc[qb][v];
+                sacc[qb] = E::mfma32(ka[0], qreg[qb][0], f32x16{});
+    #pragma unroll
+                for (int ks = 1; ks < NKS; ++ks) sacc[qb] = E::mfma32(ka[ks], qreg[qb][ks], sacc[qb]);
+            }
+        };
+
+        // One 32-key block.  sc holds this block's S^T, sn receives the next block's; the two
+        // are distinct registers (the caller alternates them), so the next block's MFMAs carry
+        // no register dependence on this block's exponentials and can overlap them.
+        auto block = [&](int j, int kb, f32x16 (&sc)[kQB], f32x16 (&sn)[kQB]) {
+            const uint16_t* Ks = lds + (j & 1) * STAGE;
+            const uint16_t* Vs = Ks + BC * KSTR;
+            const uint16_t* Ks_next = lds + ((j + 1) & 1) * STAGE;
+            const int bi = j * NKB + kb;
+            const int kfirst = bi * 32;
+            const bool live = bi < nb_live;            // wave-uniform
+            u32x4 va[2][NDB];
+            u32x4 ka[NKS];
+            float m_use[kQB];
+            if (live) {
+                // 1. operands
+    #pragma unroll
+                for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const uint16_t* vp = Vs + v_lane + (kb * 32 + 16 * h) * VSTR + db * 32;
+                        const u32x2 lo = read_tr(vp);
+                        const u32x2 hi = read_tr(vp + 8 * VSTR);
+                        va[h][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                    }
+                if (kb + 1 < NKB) read_k(ka, Ks, kb + 1);
+                // 2. statistics
+                const bool mask_blk = (CAUSAL && kfirst + 31 > q0w) || kfirst + 32 > N;
+    #pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) {
+                    // a5: elementwise mask (select, never multiply)
+                    if (mask_blk) {
+                        const int q = q0w + 32 * qb + l32;
+    #pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int key = kfirst + 8 * (v >> 2) + 4 * g + (v & 3);
+                            const bool masked = key >= N || (CAUSAL && key > q);
+                            sc[qb][v] = masked ? -INFINITY : sc[qb][v];
+                        }
+                    }
+                    // a6: this lane sees half of the block's keys for its row; the half
+                    // maximum decides whether the reference may stay.  Only when some lane's
+                    // half exceeds it are the two halves combined (lanes l and l^32 hold the
+                    // same row), so both halves always agree on m_ref.
+                    float mloc = fmaxf(fmaxf(sc[qb][0], sc[qb][1]), sc[qb][2]);
+    #pragma unroll
+                    for (int v = 3; v < 16; ++v) mloc = fmaxf(mloc, sc[qb][v]);
+                    if (__ballot(mloc * scale_log2 > m_ref[qb] + kRescaleSlack)) {
+                        const float m_blk = fmaxf(mloc, xor_lanes(mloc, 32)) * scale_log2;
+                        const bool move = m_blk > m_ref[qb] + kRescaleSlack;
+                        const float m_new = move ? m_blk : m_ref[qb];
+                        const float alpha = fast_exp2(m_ref[qb] - m_new);   // 0 on the first block
+                        l_run[qb] *= alpha;
+    #pragma unroll
+                        for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+                        m_ref[qb] = m_new;
+                    }
+                    m_use[qb] = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
+                }
+            }
+            // 3. tile boundary
+            if (kb == NKB - 1) {
+                if (j + 1 < n_kv) store_tile((j + 1) & 1);
+                __syncthreads();
+                if (j + 2 < n_kv) load_tile(j + 2);
+                if (live) read_k(ka, Ks_next, 0);
+            }
+            // 4. next S^T, this block's weights and O^T update
+            if (live) {
+                s_product(ka, sn);
+    #pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) {
+                    float p[16];
+    #pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        p[v] = fast_exp2(__builtin_fmaf(sc[qb][v], scale_log2, -m_use[qb]));
+                    float lsum = 0.f;
+    #pragma unroll
+                    for (int v = 0; v < 16; ++v) lsum += p[v];
+                    l_run[qb] += lsum;
+                    // a7: O^T += V^T P^T over the block's two 16-key steps
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const u32x4 pk = {E::pack2(p[8 * h + 0], p[8 * h + 1]),
+                                          E::pack2(p[8 * h + 2], p[8 * h + 3]),
+                                          E::pack2(p[8 * h + 4], p[8 * h + 5]),
+                                          E::pack2(p[8 * h + 6], p[8 * h + 7])};
+    #pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            oacc[qb][db] = E::mfma32(va[h][db], pk, oacc[qb][db]);
                     }
                 }
-                // a6: this lane sees half of the block's keys for its row; the half
-                // maximum decides whether the reference may stay.  Only when some lane's
-                // half exceeds it are the two halves combined (lanes l and l^32 hold the
-                // same row), so both halves always agree on m_ref.
-                float mloc = fmaxf(fmaxf(sc[qb][0], sc[qb][1]), sc[qb][2]);
-#pragma unroll
-                for (int v = 3; v < 16; ++v) mloc = fmaxf(mloc, sc[qb][v]);
-                if (__ballot(mloc * scale_log2 > m_ref[qb] + kRescaleSlack)) {
-                    const float m_blk = fmaxf(mloc, xor_lanes(mloc, 32)) * scale_log2;
-                    const bool move = m_blk > m_ref[qb] + kRescaleSlack;
-                    const float m_new = move ? m_blk : m_ref[qb];
-                    const float alpha = fast_exp2(m_ref[qb] - m_new);   // 0 on the first block
-                    l_run[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
-                    m_ref[qb] = m_new;
+            }
+        };
+
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+        if (n_kv > 1) load_tile(1);
+
+        static_assert(NKB == 2, "the block loop alternates two score buffers over two blocks per tile");
+        f32x16 s_a[kQB], s_b[kQB];
+        if (nb_live > 0) {
+            u32x4 ka[NKS];
+            read_k(ka, lds, 0);
+            s_product(ka, s_a);
+        }
+        for (int j = 0; j < n_kv; ++j) {
+            block(j, 0, s_a, s_b);
+            block(j, 1, s_b, s_a);
+        }
+
+        // a8: epilogue -- O = O~ / l, LSE = (m_ref + log2 l) ln 2
+    #pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int q = q0w + 32 * qb + l32;
+            if (q >= N) continue;
+            const float l_tot = l_run[qb] + xor_lanes(l_run[qb], 32);
+            const float inv_l = 1.f / l_tot;
+            uint16_t* orow = O + (qh_off + q) * D;
+    #pragma unroll
+            for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x16& o = oacc[qb][db];
+                    const u32x2 w = {E::pack2(o[4 * a + 0] * inv_l, o[4 * a + 1] * inv_l),
+                                     E::pack2(o[4 * a + 2] * inv_l, o[4 * a + 3] * inv_l)};
+                    *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
                 }
-                m_use[qb] = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
-            }
+            if (g == 0) LSE[qh_off + q] = (m_ref[qb] + fast_log2(l_tot)) * kLn2;
         }
-        // 3. tile boundary
-        if (kb == NKB - 1) {
-            if (j + 1 < n_kv) store_tile((j + 1) & 1);
-            __syncthreads();
-            if (j + 2 < n_kv) load_tile(j + 2);
-            if (live) read_k(ka, Ks_next, 0);
-        }
-        // 4. next S^T, this block's weights and O^T update
-        if (live) {
-            s_product(ka, sn);
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                float p[16];
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    p[v] = fast_exp2(__builtin_fmaf(sc[qb][v], scale_log2, -m_use[qb]));
-                float lsum = 0.f;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) lsum += p[v];
-                l_run[qb] += lsum;
-                // a7: O^T += V^T P^T over the block's two 16-key steps
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const u32x4 pk = {E::pack2(p[8 * h + 0], p[8 * h + 1]),
-                                      E::pack2(p[8 * h + 2], p[8 * h + 3]),
-                                      E::pack2(p[8 * h + 4], p[8 * h + 5]),
-                                      E::pack2(p[8 * h + 6], p[8 * h + 7])};
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        oacc[qb][db] = E::mfma32(va[h][db], pk, oacc[qb][db]);
-                }
-            }
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    if (n_kv > 1) load_tile(1);
-
-    static_assert(NKB == 2, "the block loop alternates two score buffers over two blocks per tile");
-    f32x16 s_a[kQB], s_b[kQB];
-    if (nb_live > 0) {
-        u32x4 ka[NKS];
-        read_k(ka, lds, 0);
-        s_product(ka, s_a);
-    }
-    for (int j = 0; j < n_kv; ++j) {
-        block(j, 0, s_a, s_b);
-        block(j, 1, s_b, s_a);
-    }
-
-    // a8: epilogue -- O = O~ / l, LSE = (m_ref + log2 l) ln 2
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const int q = q0w + 32 * qb + l32;
-        if (q >= N) continue;
-        const float l_tot = l_run[qb] + xor_lanes(l_run[qb], 32);
-        const float inv_l = 1.f / l_tot;
-        uint16_t* orow = O + (qh_off + q) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const f32x16& o = oacc[qb][db];
-                const u32x2 w = {E::pack2(o[4 * a + 0] * inv_l, o[4 * a + 1] * inv_l),
-                                 E::pack2(o[4 * a + 2] * inv_l, o[4 * a + 3] * inv_l)};
-                *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
-            }
-        if (g == 0) LSE[qh_off + q] = (m_ref[qb] + fast_log2(l_tot)) * kLn2;
+        if (!PERSIST) break;
     }
 }
 
@@ -362,12 +384,28 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     constexpr int kBR = 32 * PrefillTile<D>::QB * kWaves;
     const int n_qtiles = (a.N + kBR - 1) / kBR;
     const int n_hg = a.B * a.Hkv;
-    const long long grid = (long long)n_qtiles * a.B * a.Hq;
+    const long long n_items = (long long)n_qtiles * a.B * a.Hq;
     const int xcd_major = (n_hg % 8 == 0) ? 1 : 0;
+    // Short sequences: a persistent grid, one workgroup per resident slot (OCC per CU), so
+    // CUs do not idle between short workgroups.  Long ones: one workgroup per item; there the
+    // dispatcher's dynamic hand-out evens out the workgroups' different speeds.
+#ifdef PREFILL_PERSISTENT
+    const bool persistent = PREFILL_PERSISTENT;
+#else
+    const bool persistent = a.N <= 2048;
+#endif
+    const long long slots = (long long)device_cu_count() * PrefillTile<D>::OCC;
+    const long long grid = persistent && n_items > slots ? slots : n_items;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL>, dim3((unsigned)grid),
+    if (grid < n_items)
+        return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, true>, dim3((unsigned)grid),
+                             dim3(kThreads), (hipStream_t)a.stream, "prefill_fwd_kernel", a.Q,
+                             a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N, scale_log2, n_qtiles,
+                             (int)n_items, xcd_major);
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false>, dim3((unsigned)grid),
                          dim3(kThreads), (hipStream_t)a.stream, "prefill_fwd_kernel", a.Q, a.K,
-                         a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N, scale_log2, n_qtiles, xcd_major);
+                         a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N, scale_log2, n_qtiles,
+                         (int)n_items, xcd_major);
 }
 
 }  // namespace

@@ -62,6 +62,54 @@ def test_prefill_small_all_elements(B, Hq, Hkv, N, d, causal, dtype):
     assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, "prefill")
 
 
+# Short sequences with more query tiles than resident workgroup slots (768 at d = 64, 512 at
+# d = 128) run on the persistent grid, where one workgroup takes several items in turn.
+PERSISTENT = [
+    (16, 16, 16, 400, 64, True, BF16),
+    (8, 16, 4, 520, 128, True, FP16),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,dtype", PERSISTENT)
+def test_prefill_persistent_grid_all_elements(B, Hq, Hkv, N, d, causal, dtype):
+    say(f"prefill persistent B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal{causal} dtype{dtype}")
+    case = prefill_case(B, Hq, Hkv, N, d, causal, dtype, seeds=(11, 12, 13))
+    O, LSE = run_fwd(case)
+    O_ref, L_ref = oracle.attention(case.q, case.k, case.v, causal, case.scale, dtype)
+    assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, "prefill persistent")
+
+
+def test_prefill_repeated_and_concurrent_launches_agree_bitwise():
+    # Back-to-back runs and runs on two streams at once (the persistent grid) give identical
+    # bits: the kernel keeps no state between launches.
+    import exact_attention_08_amd as attn
+    say("prefill repeated/concurrent launches")
+    case = prefill_case(16, 16, 16, 400, 64, True, BF16, seeds=(14, 15, 16))
+    Q, K, V = (to_dev(x, case.dtype) for x in (case.q, case.k, case.v))
+    outs = []
+    for _ in range(3):
+        O = torch.empty_like(Q)
+        L = torch.empty(case.B, case.Hq, case.N, dtype=torch.float32, device="cuda")
+        attn.attn_fwd(Q, K, V, O, L, case.causal, case.scale)
+        outs.append((O, L))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for st in streams:
+        O = torch.empty_like(Q)
+        L = torch.empty(case.B, case.Hq, case.N, dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(st):
+            attn.attn_fwd(Q, K, V, O, L, case.causal, case.scale, stream=st)
+        outs.append((O, L))
+    torch.cuda.synchronize()
+    for O, L in outs[1:]:
+        assert torch.equal(O, outs[0][0]) and torch.equal(L, outs[0][1])
+    rows = np.arange(0, case.B * case.Hq * case.N, 997, dtype=np.int64)
+    O_ref, L_ref = oracle.attention(case.q, case.k, case.v, True, case.scale, BF16, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    assert_parity(from_dev_f64(outs[0][0].view(-1, case.d)[idx]), O_ref,
+                  outs[0][1].view(-1)[idx].cpu().numpy(), L_ref, "repeated")
+
+
 @pytest.mark.parametrize("N,d,causal", [(1, 64, True), (200, 128, True), (333, 64, False),
                                         (1024, 128, True)])
 def test_prefill_zero_queries_count_visible_keys(N, d, causal):
