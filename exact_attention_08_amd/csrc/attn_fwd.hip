@@ -17,27 +17,30 @@
 // are the same quantities as with the per-block rescale.
 //
 // MI355X mapping (not the pages' CUDA design):
-//   * 4 waves per workgroup, two waves per SIMD.  A wave owns QB column blocks of 32 query
-//     rows (QB = 1 at d = 128, 2 at d = 64; BR = 128 * QB).  It computes
-//     S^T = K_j Q_i^T with v_mfma_f32_32x32x16: keys are the MFMA rows and queries its
-//     columns, so one lane holds 16 scores of ONE query row per 32-key block.  Row max /
-//     row sum are in-lane reductions plus one exchange with the lane 32 away; the
-//     exponentiated scores, rounded to 16 bits, are already the B operand of
-//     O^T = V_j^T P^T, so P never leaves registers, and the rescale factor is a per-lane
-//     scalar.  With two column blocks every K or V operand read from LDS feeds two
-//     products.
-//   * A KV tile is processed as 32-key blocks; the next block's K operands and the current
-//     block's V operands are read from LDS ahead of their use.
+//   * 4 waves per workgroup, one 32-row query block per wave (BR = 128 rows); 2 waves per
+//     SIMD at d = 128, 3 at d = 64.  A wave computes S^T = K_j Q_i^T with
+//     v_mfma_f32_32x32x16: keys are the MFMA rows and queries its columns, so one lane holds
+//     16 scores of ONE query row per 32-key block.  Row max / row sum are in-lane reductions
+//     plus one exchange with the lane 32 away; the exponentiated scores, rounded to 16 bits,
+//     are already the B operand of O^T = V_j^T P^T, so P never leaves registers, and the
+//     rescale factor is a per-lane scalar.
+//   * The KV sweep is a software pipeline over 32-key blocks: the next block's S^T MFMAs are
+//     issued in the same branch-free region as this block's exponentials and O^T MFMAs
+//     (two alternating score buffers, so they carry no register dependence), and operands
+//     are read from LDS one step ahead of their use.
 //   * Q stays in registers for the whole KV sweep (B operand of the first product).
-//   * K_j is staged row-major in LDS, V_j transposed (d-major) with the key order inside
-//     each 16-key chunk permuted so every MFMA operand is one 16-byte LDS read; rows are
-//     padded by 16 bytes (bank-conflict free).  LDS is double buffered: one barrier per
-//     tile, and the next tile is fetched from HBM into registers during the math.
+//   * K_j and V_j are staged row-major in LDS (rows padded so the reads below are
+//     bank-conflict free).  K operands are 16-byte LDS reads; the transposed V operand comes
+//     from the transposing LDS read (ds_read_b64_tr_b16), so staging needs no shuffles.
+//     LDS is double buffered: one barrier per 64-key tile, and the next tile is fetched from
+//     HBM into registers during the math.
 //   * All HBM reads are buffer loads whose range is the head's rows, so rows past N read as
 //     zero without any branch.
 //   * exp2 / log2 run on v_exp_f32 / v_log_f32 with log2(e) folded into the score scale.
 //   * Work order: the query heads sharing one K/V head, and all their query tiles, run on
-//     one XCD (one L2), heaviest causal tile first.
+//     one XCD (one L2), heaviest causal tile first.  Short sequences use a persistent grid
+//     (one workgroup per resident slot taking items in turn), long ones one workgroup per
+//     item.
 #include "attn_common.h"
 #include "attn_internal.h"
 
