@@ -24,6 +24,11 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
+# Per-source extra flags.  The decode kernel's atomics are all issued by a single lane and
+# their results are needed only much later; the compiler's atomic optimizer would expand
+# each into a wave-wide broadcast that reads the result at once (a wait on every load in
+# flight), so it is off for that file.
+EXTRA_FLAGS = {"attn_decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -32,7 +37,8 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [HIPCC, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

@@ -28,6 +28,7 @@
 //   * The 4 waves of a workgroup take every 4th page of the item; their states are merged
 //     through LDS at the end of the item.
 #include <algorithm>
+#include <atomic>
 
 #include "attn_common.h"
 #include "attn_internal.h"
@@ -36,15 +37,26 @@ namespace attn {
 namespace {
 
 constexpr int kPage = 16;
+constexpr int kLoadNT = 2;   // cache-policy operand of a buffer load: non-temporal
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
+
+// Work queues of the split kernel: per launch slot, [0] the next ticket and [1] the number
+// of workgroups that have finished.  The last workgroup of a launch to finish puts the slot
+// back to zero, so it is ready for a later launch without any host-side reset.
+constexpr int kDecSchedSlots = 64;
+// Batches up to this size keep their per-sequence split counts in LDS (built once per
+// workgroup), so finding an item's sequence needs no global loads.
+constexpr int kSeqCache = 1024;
+__device__ unsigned g_decode_sched[kDecSchedSlots][4];
 
 template <int D, bool IS_BF16>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kp,
     const uint16_t* __restrict__ Vp, const int* __restrict__ block_table,
     const int* __restrict__ ctx_lens, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    int B, int Hq, int Hkv, int max_pages, int split_tokens, int S_max, float scale_log2) {
+    int B, int Hq, int Hkv, int max_pages, int split_tokens, int S_max, float scale_log2,
+    int sched_slot) {
     using E = Elem<IS_BF16>;
     constexpr int NKS = D / 32;          // k-steps of S^T = K Q^T (32 dims each)
     constexpr int NDB = D / 16;          // 16-row d blocks of O^T
@@ -56,6 +68,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     constexpr int LDS_BYTES_MERGE = kDecWaves * 16 * (D + 2) * 4;
     constexpr int LDS_BYTES = LDS_BYTES_V > LDS_BYTES_MERGE ? LDS_BYTES_V : LDS_BYTES_MERGE;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    __shared__ int s_ticket;
+    __shared__ int s_pref[2][kSeqCache];   // inclusive prefix sums: full splits, partial splits
+    __shared__ int s_ctx[kSeqCache];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -76,15 +91,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const int v_dc = (lane >> 2) & (KCH - 1);
     const int vofs_v = (4 * v_tg * (int)row_stride + v_dc * 8) * 2;
 
-    // Work list.  The non-empty items (sequence r, split s, kv head) are numbered
-    // f = t * Hkv + kvh, where t runs over the splits of sequence 0, then of sequence 1, ...
-    // (ceil(ctx_r / split_tokens) splits each).  Workgroup b takes items b, b + gridDim.x,
-    // ...; the loop ends for every wave once f passes the item count, so the grid always
-    // drains.  Each wave derives the count and its item's (r, s) from ctx_lens with
-    // wave-wide prefix sums over chunks of 64 sequences (all results are wave-uniform).
-    auto n_split_of = [&](int rr) {
-        return rr < B ? (ctx_lens[rr] + split_tokens - 1) / split_tokens : 0;
-    };
+    // Work list.  The non-empty splits are numbered t = 0 .. n_full + n_part - 1: first the
+    // full splits (split_tokens tokens) of sequence 0, 1, ..., then the shorter last split of
+    // every sequence whose length is not a multiple of split_tokens, so the queue ends with
+    // its lightest items.  Item f = t * Hkv + kvh.  Workgroups draw items from an atomic
+    // ticket counter (faster workgroups take more); a workgroup leaves once its ticket passes
+    // the item count, so the grid always drains.  Each wave derives the counts and an item's
+    // (r, split) from ctx_lens with wave-wide prefix sums over chunks of 64 sequences (all
+    // results are wave-uniform).
+    auto n_full_of = [&](int rr) { return rr < B ? ctx_lens[rr] / split_tokens : 0; };
+    auto n_part_of = [&](int rr) { return rr < B && ctx_lens[rr] % split_tokens != 0 ? 1 : 0; };
     auto incl_scan = [&](int v) {
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -93,76 +109,161 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         }
         return v;
     };
-    int total_splits = 0;
-    for (int c0 = 0; c0 < B; c0 += 64) total_splits += __shfl(incl_scan(n_split_of(c0 + lane)), 63, 64);
-    const int n_items = __builtin_amdgcn_readfirstlane(total_splits) * Hkv;
+    auto total_of = [&](auto count) {
+        int tot = 0;
+        for (int c0 = 0; c0 < B; c0 += 64) tot += __shfl(incl_scan(count(c0 + lane)), 63, 64);
+        return __builtin_amdgcn_readfirstlane(tot);
+    };
+    // the sequence holding the t-th unit of `count`, and the unit's index inside it
+    auto locate = [&](auto count, int t, int& r_out, int& k_out) {
+        int base = 0;
+        for (int c0 = 0; c0 < B; c0 += 64) {
+            const int n = count(c0 + lane);
+            const int inc = incl_scan(n);
+            const int tot = __shfl(inc, 63, 64);
+            if (t < base + tot) {
+                const int exc = base + inc - n;
+                const unsigned long long hit = __ballot(n > 0 && exc <= t && t < base + inc);
+                const int lr = __builtin_ctzll(hit);
+                r_out = c0 + lr;
+                k_out = t - __shfl(exc, lr, 64);
+                return;
+            }
+            base += tot;
+        }
+    };
+    const int n_full = total_of(n_full_of);
+    const int n_items = (n_full + total_of(n_part_of)) * Hkv;
+    unsigned* const queue = g_decode_sched[sched_slot];
 
-    for (int f = blockIdx.x; f < n_items; f += gridDim.x) {
-        const int t_item = f / Hkv;
-        const int kvh = f % Hkv;
-        int r = 0, split = 0;
-        {
-            int base = 0;
+    const bool cached = B <= kSeqCache;
+    if (cached) {
+        if (wave == 0) {
+            int base_f = 0, base_p = 0;
             for (int c0 = 0; c0 < B; c0 += 64) {
-                const int n = n_split_of(c0 + lane);
-                const int inc = incl_scan(n);
-                const int tot = __shfl(inc, 63, 64);
-                if (t_item < base + tot) {
-                    const int exc = base + inc - n;
-                    const unsigned long long hit =
-                        __ballot(n > 0 && exc <= t_item && t_item < base + inc);
-                    const int lr = __builtin_ctzll(hit);
-                    r = c0 + lr;
-                    split = t_item - __shfl(exc, lr, 64);
-                    break;
+                const int rr = c0 + lane;
+                const int inc_f = incl_scan(n_full_of(rr)) + base_f;
+                const int inc_p = incl_scan(n_part_of(rr)) + base_p;
+                if (rr < B) {
+                    s_pref[0][rr] = inc_f;
+                    s_pref[1][rr] = inc_p;
+                    s_ctx[rr] = ctx_lens[rr];
                 }
-                base += tot;
+                base_f = __shfl(inc_f, 63, 64);
+                base_p = __shfl(inc_p, 63, 64);
             }
         }
-        r = __builtin_amdgcn_readfirstlane(r);
-        split = __builtin_amdgcn_readfirstlane(split);
-        const int ctx = ctx_lens[r];
-        const int tok0 = split * split_tokens;
-        const int tok_end = min(ctx, tok0 + split_tokens);
-        const int page0 = tok0 / kPage;
-        const int n_pages = (tok_end - tok0 + kPage - 1) / kPage;
-        const int* bt = block_table + (int64_t)r * max_pages + page0;
-        const uint16_t* Kh = Kp + (int64_t)kvh * D;   // kv-head column of the pools
-        const uint16_t* Vh = Vp + (int64_t)kvh * D;
-
-        // query heads of this kv head as the B operand (column = head l16); lanes past the
-        // group read a valid head and are zeroed
-        u32x4 qreg[NKS];
-        {
-            const int head = kvh * G + min(l16, G - 1);
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const u32x4 t = ldg16(q + ((int64_t)r * Hq + head) * D + ks * 32 + g4 * 8);
-                qreg[ks] = (l16 < G) ? t : zero4();
-            }
+        __syncthreads();
+    }
+    // the sequence holding unit t of the cached prefix array pf (the first r with pf[r] > t)
+    auto find_cached = [&](const int* pf, int t) {
+        for (int c0 = 0;; c0 += 64) {
+            const int v = c0 + lane < B ? pf[c0 + lane] : 0x7fffffff;
+            const unsigned long long hit = __ballot(v > t);
+            if (hit) return __builtin_amdgcn_readfirstlane(c0 + __builtin_ctzll(hit));
         }
+    };
 
+    // One work item: sequence r, split, kv head, and this wave's share of its pages.
+    // An item past the end of the list (valid == false) reads nothing.
+    struct Item {
+        int r, split, kvh, tok0, tok_end, n_pages, cnt;
+        bool valid;
+        const int* bt;
+    };
+    auto setup = [&](int ff) {
+        Item it;
+        it.valid = ff < n_items;
+        const int fv = it.valid ? ff : 0;
+        const int t_item = fv / Hkv;
+        it.kvh = fv % Hkv;
+        int r = 0, split = 0, ctx = 0;
+        if (cached) {
+            if (t_item < n_full) {
+                r = find_cached(s_pref[0], t_item);
+                split = t_item - (r > 0 ? s_pref[0][r - 1] : 0);
+                ctx = (split + 1) * split_tokens;   // a full split: its end is inside ctx
+            } else {
+                r = find_cached(s_pref[1], t_item - n_full);
+                split = s_pref[0][r] - (r > 0 ? s_pref[0][r - 1] : 0);   // its full splits
+                ctx = s_ctx[r];
+            }
+        } else {
+            if (t_item < n_full) {
+                locate(n_full_of, t_item, r, split);
+            } else {
+                locate(n_part_of, t_item - n_full, r, split);
+                split = ctx_lens[__builtin_amdgcn_readfirstlane(r)] / split_tokens;
+            }
+            ctx = ctx_lens[__builtin_amdgcn_readfirstlane(r)];
+        }
+        it.r = __builtin_amdgcn_readfirstlane(r);
+        it.split = __builtin_amdgcn_readfirstlane(split);
+        ctx = __builtin_amdgcn_readfirstlane(ctx);
+        it.tok0 = it.split * split_tokens;
+        it.tok_end = min(ctx, it.tok0 + split_tokens);
+        it.n_pages = (it.tok_end - it.tok0 + kPage - 1) / kPage;
         // pages of this wave: lp = wave + 4*i, i < cnt
-        const int cnt = wave < n_pages ? (n_pages - wave + kDecWaves - 1) / kDecWaves : 0;
+        it.cnt = (it.valid && wave < it.n_pages)
+                     ? (it.n_pages - wave + kDecWaves - 1) / kDecWaves : 0;
+        it.bt = block_table + (int64_t)it.r * max_pages + it.tok0 / kPage;
+        return it;
+    };
 
-        struct Page { u32x4 k[NKS]; u32x4 v[4]; };
-        // Page i of this wave (clamped to the wave's last page, so a prefetch past the end
-        // re-reads a page that is already cached).  Every load is inside the page.
-        auto load_page = [&](Page& P, int i) {
-            const int lp = __builtin_amdgcn_readfirstlane(wave + kDecWaves * min(i, cnt - 1));
-            const int phys = bt[lp];
-            const int64_t pofs = (int64_t)phys * kPage * row_stride;
-            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(Kh + pofs), (short)0, page_bytes, 0x00020000);
-            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(Vh + pofs), (short)0, page_bytes, 0x00020000);
+    // query heads of the item's kv head as the B operand (column = head l16).  The
+    // descriptor covers exactly the G heads of the group, so lanes past it read zeros; no
+    // select on the loaded value means nothing waits for these loads before the first
+    // product that uses them.
+    u32x4 qreg[NKS];
+    const int q_vofs = (l16 * D + g4 * 8) * 2;
+    auto load_q = [&](const Item& it) {
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(q + ((int64_t)it.r * Hq + it.kvh * G) * D), (short)0, G * D * 2, 0x00020000);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                P.k[ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, vofs_k, ks * 64, 0);
+        for (int ks = 0; ks < NKS; ++ks)
+            qreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_vofs + ks * 64, 0, 0);
+    };
+
+    struct Page { u32x4 k[NKS]; u32x4 v[4]; };
+    // Page i of this wave's share of item it.  Past the share (a prefetch beyond the last
+    // page, or an invalid item) the descriptors have length 0: nothing is read and the
+    // registers receive zeros.  The loads are issued either way, so the wait counter sees
+    // the same outstanding loads on every path.
+    auto load_page = [&](const Item& it, Page& P, int i) {
+        const bool inside = i < it.cnt;                       // wave-uniform
+        const int lp = __builtin_amdgcn_readfirstlane(wave + kDecWaves * (inside ? i : 0));
+        const int phys = inside ? it.bt[lp] : 0;
+        const int64_t pofs = (int64_t)phys * kPage * row_stride + (int64_t)it.kvh * D;
+        const int len = inside ? page_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Kp + pofs), (short)0, len, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Vp + pofs), (short)0, len, 0x00020000);
+        // Every K/V byte is read exactly once: the loads are marked non-temporal (nt), so
+        // they stream past the caches instead of displacing what is reused.
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                P.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, vofs_v, e * slot_bytes, 0);
-        };
+        for (int ks = 0; ks < NKS; ++ks)
+            P.k[ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, vofs_k + ks * 64, 0, kLoadNT);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            P.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, vofs_v + e * slot_bytes, 0, kLoadNT);
+    };
+
+    if (tid == 0) s_ticket = (int)atomicAdd(&queue[0], 1u);
+    __syncthreads();
+    int f = s_ticket;
+    Item it = setup(f);
+    Page b0, b1, b2;
+    load_q(it);
+    load_page(it, b0, 0);
+    load_page(it, b1, 1);
+    while (f < n_items) {
+        // The next item's ticket is drawn by thread 0 now, after this item's first two page
+        // loads were issued (so waiting for those loads does not wait for the atomic), and
+        // published at the cross-wave merge below.  It has no value on the other threads, so
+        // nothing waits for the atomic before that point.
+        int next_ticket;
+        if (tid == 0) next_ticket = (int)atomicAdd(&queue[0], 1u);
 
         float m_run = -INFINITY, l_run = 0.f;
         f32x4 oacc[NDB];
@@ -170,15 +271,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
 
         auto compute_page = [&](const Page& P, int i) {
-            const int t_pg = tok0 + (wave + kDecWaves * i) * kPage;   // first token of the page
-            const bool tail = t_pg + kPage > tok_end;                 // wave-uniform
+            const int t_pg = it.tok0 + (wave + kDecWaves * i) * kPage;   // first token of the page
+            const bool tail = t_pg + kPage > it.tok_end;                 // wave-uniform
             // S^T: rows = slots 4*g4 + v, column = head l16
             f32x4 s = f32x4{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) s = E::mfma16(P.k[ks], qreg[ks], s);
             if (tail) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) s[v] = (t_pg + 4 * g4 + v < tok_end) ? s[v] : -INFINITY;
+                for (int v = 0; v < 4; ++v) s[v] = (t_pg + 4 * g4 + v < it.tok_end) ? s[v] : -INFINITY;
             }
             // V^T into the slab (zeros for slots past the context)
 #pragma unroll
@@ -186,7 +287,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
                 uint32_t w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    w[e] = (!tail || t_pg + 4 * v_tg + e < tok_end) ? P.v[e][p] : 0u;
+                    w[e] = (!tail || t_pg + 4 * v_tg + e < it.tok_end) ? P.v[e][p] : 0u;
                 const int d = v_dc * 8 + 2 * p;
                 *reinterpret_cast<u32x2*>(&slab[d * VSTR + 4 * v_tg]) =
                     pack_col_lo(w[0], w[1], w[2], w[3]);
@@ -226,24 +327,22 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         };
 
         // Page sweep: three register sets in rotation, two pages in flight ahead of the one
-        // being computed.  The prefetch is unconditional (clamped), so the wait counter
-        // sees the same outstanding loads on every path.
+        // being computed.
+        const int cnt = it.cnt;
         if (cnt > 0) {
-            Page b0, b1, b2;
-            load_page(b0, 0);
-            load_page(b1, 1);
             for (int i = 0;;) {
-                load_page(b2, i + 2);
+                load_page(it, b2, i + 2);
                 compute_page(b0, i);
                 if (++i >= cnt) break;
-                load_page(b0, i + 2);
+                load_page(it, b0, i + 2);
                 compute_page(b1, i);
                 if (++i >= cnt) break;
-                load_page(b1, i + 2);
+                load_page(it, b1, i + 2);
                 compute_page(b2, i);
                 if (++i >= cnt) break;
             }
         }
+        if (tid == 0) s_ticket = next_ticket;
 
         // per-head totals of this wave: l over the 4 lane groups
         float l_w = l_run + xor_lanes(l_run, 16);
@@ -251,6 +350,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
 
         // cross-wave merge through LDS (slabs are dead now)
         __syncthreads();
+        const int f_next = s_ticket;
+        // The next item's Q and first two pages load while this item is merged (the page
+        // registers and Q are free now), so HBM stays busy across the item boundary.
+        const Item nx = setup(f_next);
+        load_q(nx);
+        load_page(nx, b0, 0);
+        load_page(nx, b1, 1);
         float* mbuf = reinterpret_cast<float*>(lds);                 // [4][16]
         float* lbuf = mbuf + kDecWaves * 16;                          // [4][16]
         float* obuf = lbuf + kDecWaves * 16;                          // [4][16][D]
@@ -265,7 +371,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
                 obuf[(wave * 16 + l16) * D + db * 16 + 4 * g4 + v] = oacc[db][v];
         __syncthreads();
 
-        const int64_t part = ((int64_t)r * Hq + kvh * G) * S_max;   // (r, first head) partials
+        const int64_t part = ((int64_t)it.r * Hq + it.kvh * G) * S_max;   // (r, first head) partials
         for (int e = tid; e < G * D; e += kDecThreads) {
             const int hh = e / D, d = e % D;
             float m = -INFINITY;
@@ -278,11 +384,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
                 lt += wt * lbuf[w * 16 + hh];
                 ot += wt * obuf[(w * 16 + hh) * D + d];
             }
-            const int64_t pidx = part + (int64_t)hh * S_max + split;
+            const int64_t pidx = part + (int64_t)hh * S_max + it.split;
             ws_o[pidx * D + d] = ot / lt;
             if (d == 0) ws_lse[pidx] = (m + fast_log2(lt)) * kLn2;
         }
         __syncthreads();   // merge buffers fully read before the next item reuses the LDS
+        f = f_next;
+        it = nx;
+    }
+    // the last workgroup to finish resets the queue slot for a later launch
+    if (tid == 0) {
+        __threadfence();
+        if (atomicAdd(&queue[1], 1u) == gridDim.x - 1) {
+            atomicExch(&queue[0], 0u);
+            atomicExch(&queue[1], 0u);
+        }
     }
 }
 
@@ -328,10 +444,16 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     const long long max_items = (long long)a.B * S * a.Hkv;
     const long long grid = std::min<long long>(max_items, 2LL * device_cu_count());
+    // each launch takes the next queue slot; concurrent launches (different streams) use
+    // different slots as long as fewer than kDecSchedSlots are in flight on one device
+    static std::atomic<unsigned> launch_seq{0};
+    const int sched_slot =
+        (int)(launch_seq.fetch_add(1, std::memory_order_relaxed) % kDecSchedSlots);
     hipError_t e = launch_kernel(decode_split_kernel<D, IS_BF16>, dim3((unsigned)grid),
                                  dim3(kDecThreads), st, "decode_split_kernel", a.q, a.Kpages,
                                  a.Vpages, a.block_table, a.ctx_lens, ws_o, ws_lse, a.B, a.Hq,
-                                 a.Hkv, a.max_pages, a.split_tokens, (int)S, scale_log2);
+                                 a.Hkv, a.max_pages, a.split_tokens, (int)S, scale_log2,
+                                 sched_slot);
     if (e != hipSuccess) return e;
     return launch_kernel(decode_merge_kernel<D, IS_BF16>, dim3((unsigned)(a.B * a.Hq)), dim3(D),
                          st, "decode_merge_kernel", ws_o, ws_lse, a.ctx_lens, a.O, a.LSE, a.Hq,
