@@ -13,9 +13,10 @@
 //     O = sum e^{LSE_s - LSE} O_s.
 //
 // MI355X mapping:
-//   * A fixed grid of 2 workgroups per CU walks the list of non-empty work items (the list
-//     is derived on the fly from ctx_lens), so no workgroup is launched for a split past a
-//     sequence's context.
+//   * A fixed grid of 2 workgroups per CU draws work items (sequence, split, kv head) from
+//     an atomic ticket counter, full splits first and the shorter last splits at the end,
+//     so faster workgroups take more items and the grid finishes together.  No workgroup is
+//     launched for a split past a sequence's context.
 //   * The G query heads are the columns of v_mfma_f32_16x16x32 (G <= 16), the 16 slots of
 //     a page its rows: S^T = K Q^T runs on the matrix cores with K loaded from HBM straight
 //     into the A operand.  The exponentiated scores of a page are exactly the B operand of
@@ -23,8 +24,9 @@
 //   * V is transposed through a small per-wave LDS slab (d-major); slots at or past the
 //     context length are written as zeros, so poisoned slots never reach the sum.
 //   * Each page is addressed through a buffer descriptor (page base in SGPRs, one VGPR of
-//     per-lane offset); block-table entries are scalar loads.  Each wave keeps two pages in
-//     flight ahead of the one it computes.
+//     per-lane offset); block-table entries are scalar loads; K/V loads are non-temporal.
+//     Each wave keeps two pages in flight ahead of the one it computes, and the next
+//     item's first pages are loaded while the current one is merged.
 //   * The 4 waves of a workgroup take every 4th page of the item; their states are merged
 //     through LDS at the end of the item.
 #include <algorithm>
