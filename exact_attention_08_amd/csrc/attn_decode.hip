@@ -404,13 +404,20 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     }
 }
 
-// a13: fixed-order merge of the splits of one (sequence, head); one thread per dim.
+// a13: fixed-order merge of the splits of one (sequence, head); one thread per dim.  The
+// loads are spread so that none waits for another: the split LSEs are read by all threads
+// at once (split s by thread s mod D) for the maximum, then the splits go in chunks of D,
+// thread d turning split c0 + d's LSE into its weight in LDS and every thread summing its
+// dim over the chunk in ascending split order with independent loads.
 template <int D, bool IS_BF16>
 __global__ __launch_bounds__(D) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const int* __restrict__ ctx_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int split_tokens, int S_max) {
     using E = Elem<IS_BF16>;
+    constexpr int NW = D / 64;                 // waves per workgroup
+    __shared__ float s_w[D];
+    __shared__ float s_red[NW];
     const int rh = blockIdx.x;                 // r * Hq + h
     const int r = rh / Hq;
     const int d = threadIdx.x;
@@ -418,16 +425,31 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
     const int n_split = (ctx + split_tokens - 1) / split_tokens;
     const float* lse_s = ws_lse + (int64_t)rh * S_max;
     const float* o_s = ws_o + (int64_t)rh * S_max * D;
+
     float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, lse_s[s]);
+    for (int s = d; s < n_split; s += D) M = fmaxf(M, lse_s[s]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    if ((d & 63) == 0) s_red[d >> 6] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_red[w]);
+
+    const float log2e = 1.4426950408889634f;
     float wsum = 0.f, acc = 0.f;
-    if (n_split > 0) {
-        const float log2e = 1.4426950408889634f;
-        for (int s = 0; s < n_split; ++s) {
-            const float w = fast_exp2((lse_s[s] - M) * log2e);
+    for (int c0 = 0; c0 < n_split; c0 += D) {
+        const int s = c0 + d;
+        s_w[d] = s < n_split ? fast_exp2((lse_s[s] - M) * log2e) : 0.f;
+        __syncthreads();
+        const int cnt = min(D, n_split - c0);
+        const float* oc = o_s + (int64_t)c0 * D + d;
+#pragma unroll 8
+        for (int j = 0; j < cnt; ++j) {
+            const float w = s_w[j];
             wsum += w;
-            acc += w * o_s[(int64_t)s * D + d];
+            acc += w * oc[(int64_t)j * D];
         }
+        __syncthreads();
     }
     const float out = (n_split > 0) ? acc / wsum : 0.f;
     // store as 16 bits (RNE); pairs of threads cooperate through a packed write
