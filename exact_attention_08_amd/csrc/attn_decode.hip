@@ -73,6 +73,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     __shared__ int s_ticket;
     __shared__ int s_pref[2][kSeqCache];   // inclusive prefix sums: full splits, partial splits
     __shared__ int s_ctx[kSeqCache];
+    __shared__ int s_porder[64];            // batches <= 64: partial splits, largest first
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -154,6 +155,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
                 base_f = __shfl(inc_f, 63, 64);
                 base_p = __shfl(inc_p, 63, 64);
             }
+            // Batches of at most 64 sequences hand out the shorter last splits largest
+            // first, so the final tickets are the smallest items.  Lane r ranks its last
+            // split against all others (ties by sequence index), which every workgroup
+            // computes identically.
+            if (B <= 64) {
+                const int key = lane < B ? ctx_lens[lane] % split_tokens : 0;
+                int rank = 0;
+                for (int j = 0; j < 64; ++j) {
+                    const int kj = __shfl(key, j, 64);
+                    rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
+                }
+                if (key > 0) s_porder[rank] = lane;
+            }
         }
         __syncthreads();
     }
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
                 split = t_item - (r > 0 ? s_pref[0][r - 1] : 0);
                 ctx = (split + 1) * split_tokens;   // a full split: its end is inside ctx
             } else {
-                r = find_cached(s_pref[1], t_item - n_full);
+                r = B <= 64 ? s_porder[t_item - n_full] : find_cached(s_pref[1], t_item - n_full);
                 split = s_pref[0][r] - (r > 0 ? s_pref[0][r - 1] : 0);   // its full splits
                 ctx = s_ctx[r];
             }
