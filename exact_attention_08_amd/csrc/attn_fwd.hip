@@ -29,11 +29,13 @@
 //     (two alternating score buffers, so they carry no register dependence), and operands
 //     are read from LDS one step ahead of their use.
 //   * Q stays in registers for the whole KV sweep (B operand of the first product).
-//   * K_j and V_j are staged row-major in LDS (rows padded so the reads below are
-//     bank-conflict free).  K operands are 16-byte LDS reads; the transposed V operand comes
-//     from the transposing LDS read (ds_read_b64_tr_b16), so staging needs no shuffles.
-//     LDS is double buffered: one barrier per 64-key tile, and the next tile is fetched from
-//     HBM into registers during the math.
+//   * K_j and V_j go from HBM straight into LDS with buffer loads that write LDS
+//     (buffer_load ... lds): no register staging and no LDS store instructions.  Rows are
+//     unpadded; each row's 16-byte chunks are permuted by an XOR of the row index, so that the
+//     operand reads below are bank-conflict free.  K operands are 16-byte LDS reads; the
+//     transposed V operand comes from the transposing LDS read (ds_read_b64_tr_b16), so
+//     staging needs no shuffles.  LDS is double buffered: one barrier per 64-key tile, and
+//     the next tile streams into the other stage during the math.
 //   * All HBM reads are buffer loads whose range is the head's rows, so rows past N read as
 //     zero without any branch.
 //   * exp2 / log2 run on v_exp_f32 / v_log_f32 with log2(e) folded into the score scale.
@@ -41,6 +43,8 @@
 //     one XCD (one L2), heaviest causal tile first.  Short sequences use a persistent grid
 //     (one workgroup per resident slot taking items in turn), long ones one workgroup per
 //     item.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -88,6 +92,30 @@ __device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int byt
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// buffer descriptor as four dwords (base, stride 0, byte range, flags) for inline asm
+__device__ inline i32x4 head_rsrc4(const uint16_t* base, int bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32) & 0xFFFF, bytes, 0x00020000};
+}
+// 16 bytes per lane from buffer offset voff into LDS at lds_addr + 16 * lane.  Issued as
+// inline asm: the compiler then places no wait for it before later LDS reads (the kernel
+// waits on vmcnt itself before the barrier that publishes a tile).
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds_addr, int voff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+// LDS layout of a K or V tile: rows of D elements, unpadded; the 16-byte chunk c of row r
+// sits in slot c ^ swz(r) of that row.  K is read as 16 bytes of one row per lane, 16 rows
+// at a time; V by the transposing read, 8 bytes per lane over 4 rows: with these XORs
+// either read touches every LDS bank once per pass.
+template <int D> __device__ __forceinline__ int k_swz(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int v_swz(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
 template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST>
 __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -100,14 +128,14 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     constexpr int NKB = BC / 32;         // 32-key blocks per KV tile
     constexpr int NKS = D / 16;          // k-steps of the first product
     constexpr int NDB = D / 32;          // 32-wide d blocks of the output
-    constexpr int KSTR = D + 8;          // LDS row stride of K (elements)
-    constexpr int VSTR = D + 32;         // LDS row stride of V (elements)
-    constexpr int KCH = D / 8;           // 16-byte chunks per K/V row
-    constexpr int KLOADS = BC * KCH / kThreads;   // K chunks per thread
-    constexpr int STAGE = BC * (KSTR + VSTR);     // elements per LDS stage
-    static_assert(KLOADS * kThreads == BC * KCH, "K/V tile must split evenly");
+    constexpr int RB = 2 * D;            // bytes per K/V row in LDS
+    constexpr int NSLOT = D / 8;         // 16-byte chunks per row
+    constexpr int TILE_B = BC * RB;      // bytes of one K (or V) tile
+    constexpr int STAGE_B = 2 * TILE_B;  // one LDS stage: the K tile, then the V tile
+    constexpr int NDMA = TILE_B / 1024 / kWaves;   // 1 KiB wave loads per tile and wave
+    static_assert(NDMA * 1024 * kWaves == TILE_B, "K/V tile must split into 1 KiB wave loads");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGE_B];   // two stages of STAGE_B bytes
 
     const int G = Hq / Hkv;
 
@@ -140,8 +168,6 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         const int64_t kh_off = ((int64_t)wi.b * Hkv + wi.kvh) * (int64_t)N;   // row offset of (b,kvh)
         const int head_bytes = N * D * 2;
         const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + qh_off * D, head_bytes);
-        const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + kh_off * D, head_bytes);
-        const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + kh_off * D, head_bytes);
 
         const int q_tile0 = wi.qt * kBR;
         const int q0w = q_tile0 + wave * (32 * kQB);   // first query row of this wave
@@ -162,35 +188,29 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 qreg[qb][ks] = __builtin_amdgcn_raw_buffer_load_b128(
                     rq, ((q0w + 32 * qb + l32) * D + ks * 16 + g * 8) * 2, 0, 0);
 
-        // a3: register staging of one K/V tile
-        u32x4 kreg[KLOADS], vreg[KLOADS];
-
-        auto load_tile = [&](int j) {
+        // a3: K_j, V_j go from HBM straight into LDS stage st (buffer_load ... lds): wave load
+        // i writes the 1 KiB block i * kWaves + wave of the tile, lane by lane in 16-byte
+        // slots; each lane fetches the chunk that its slot holds under the swizzle.  Rows past
+        // N read as zero (buffer range).
+        const i32x4 rk4 = head_rsrc4(K + kh_off * D, head_bytes);
+        const i32x4 rv4 = head_rsrc4(V + kh_off * D, head_bytes);
+        const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)lds);
+        auto dma_tile = [&](int j, int st) {
             const int key0 = j * BC;
     #pragma unroll
-            for (int r = 0; r < KLOADS; ++r) {
-                const int c = tid + r * kThreads;
-                const int row = c / KCH, col = (c % KCH) * 8;
-                kreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((key0 + row) * D + col) * 2, 0, 0);
-            }
-    #pragma unroll
-            for (int r = 0; r < KLOADS; ++r) {
-                const int c = tid + r * kThreads;
-                const int row = c / KCH, col = (c % KCH) * 8;
-                vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((key0 + row) * D + col) * 2, 0, 0);
-            }
-        };
-        auto store_tile = [&](int stage) {
-            uint16_t* Ks = lds + stage * STAGE;
-            uint16_t* Vs = Ks + BC * KSTR;
-    #pragma unroll
-            for (int r = 0; r < KLOADS; ++r) {
-                const int c = tid + r * kThreads;
-                const int row = c / KCH, col = (c % KCH) * 8;
-                *reinterpret_cast<u32x4*>(&Ks[row * KSTR + col]) = kreg[r];
-                *reinterpret_cast<u32x4*>(&Vs[row * VSTR + col]) = vreg[r];
+            for (int i = 0; i < NDMA; ++i) {
+                const int blk = i * kWaves + wave;
+                const int p = blk * 64 + lane;
+                const int r = p / NSLOT, sl = p % NSLOT;
+                const int kofs = ((key0 + r) * D + 8 * (sl ^ k_swz<D>(r))) * 2;
+                const int vofs = ((key0 + r) * D + 8 * (sl ^ v_swz<D>(r))) * 2;
+                const uint32_t kdst = __builtin_amdgcn_readfirstlane(lds_base + st * STAGE_B + blk * 1024);
+                dma_b128(rk4, kdst, kofs);
+                dma_b128(rv4, kdst + TILE_B, vofs);
             }
         };
+        // vmcnt(0): this wave's tile loads have landed in LDS
+        auto wait_tile = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
         // a6 state, per column block (fp32, per lane = per query row; l is this lane's half
         // of the keys)
@@ -207,37 +227,53 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         // The KV sweep runs as a software pipeline over 32-key blocks.  Iteration b:
         //   1. read block b's V operands; read the next block's K operands (same tile);
         //   2. statistics of block b's scores (mask, max, the rare rescale) -- branches here;
-        //   3. at the last block of a tile: store the next tile (already in registers) into
-        //      the other LDS stage, barrier, start fetching the tile after it from HBM, and read
-        //      the next block's K operands from the new stage;
+        //   3. at the last block of a tile: wait until this wave's loads of the next tile have
+        //      landed in LDS, barrier, start the loads of the tile after it into the stage just
+        //      freed, and read the next block's K operands from the new stage;
         //   4. one branch-free region: the next block's S^T MFMAs, block b's exponentials,
         //      sums and packing, and block b's O^T MFMAs -- independent matrix and vector work
         //      the scheduler interleaves, so the softmax runs under the matrix cores.
         // Blocks whose first key lies after the wave's last row (causal) are skipped by the
-        // wave; it still takes part in the tile stores and barriers.  Near the end the "next"
+        // wave; it still takes part in the tile loads and barriers.  Near the end the "next"
         // S^T is computed on the current block and discarded, keeping step 4 branch free.
         const int nb = n_kv * NKB;
         const int nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, wave_last_q / 32 + 1) : nb);
 
-        // V^T operand of the second product from row-major V with the transposing LDS read
+        // V^T operand of the second product from V (rows in key order) with the transposing LDS read
         // (ds_read_b64_tr_b16): within each 16-lane group G, destination lane i receives, as
         // element e, the (i % 4)-th 16-bit value of the 8 bytes addressed by lane 16G + 4e + i/4.
         // Lane 16G + 4e + a therefore addresses key 4(G >> 1) + e, dims 16(G & 1) + 4a..+3 of the
         // 16-key step, and lane l = 16G + i receives dim 16(G & 1) + i (= l % 32) for keys
         // 4(G >> 1) + 0..3; a second read 8 keys further gives keys 8 + 4(G >> 1) + 0..3.  These
         // are exactly the keys, in the same order, that the lane's P operand holds.
-        const int v_lane = (4 * ((lane >> 5) & 1) + ((lane >> 2) & 3)) * VSTR + 16 * ((lane >> 4) & 1) +
-                           4 * (lane & 3);
-        auto read_tr = [&](const uint16_t* p) -> u32x2 {
+        //
+        // Per-lane byte offsets (within a stage) of the V^T operand for each 32-wide d block,
+        // and of the K operand for each k-step.  The swizzle depends only on the low row bits,
+        // which the lane fixes (V: row mod 8, K: row mod 32), so the block's row offsets are
+        // added as constants.
+        int v_off[NDB], k_off[NKS];
+        {
+            const int vr = 4 * ((lane >> 5) & 1) + ((lane >> 2) & 3);
+    #pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1) + 4 * db;
+                v_off[db] = TILE_B + vr * RB + 16 * (c ^ v_swz<D>(vr)) + 8 * (lane & 1);
+            }
+    #pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                k_off[ks] = l32 * RB + 16 * ((2 * ks + g) ^ k_swz<D>(l32));
+        }
+        const char* lds_b = reinterpret_cast<const char*>(lds);
+        auto read_tr = [&](const char* p) -> u32x2 {
             typedef short s16x4 __attribute__((ext_vector_type(4)));
             const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(p));
             return __builtin_bit_cast(u32x2, v);
         };
-        auto read_k = [&](u32x4 (&ka)[NKS], const uint16_t* Ks, int kb) {
+        auto read_k = [&](u32x4 (&ka)[NKS], int st, int kb) {
     #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                ka[ks] = *reinterpret_cast<const u32x4*>(&Ks[(kb * 32 + l32) * KSTR + ks * 16 + g * 8]);
+                ka[ks] = *reinterpret_cast<const u32x4*>(lds_b + k_off[ks] + st * STAGE_B + kb * 32 * RB);
         };
         auto s_product = [&](const u32x4 (&ka)[NKS], f32x16 (&sacc)[kQB]) {
     #pragma unroll
@@ -251,10 +287,8 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         // One 32-key block.  sc holds this block's S^T, sn receives the next block's; the two
         // are distinct registers (the caller alternates them), so the next block's MFMAs carry
         // no register dependence on this block's exponentials and can overlap them.
-        auto block = [&](int j, int kb, f32x16 (&sc)[kQB], f32x16 (&sn)[kQB]) {
-            const uint16_t* Ks = lds + (j & 1) * STAGE;
-            const uint16_t* Vs = Ks + BC * KSTR;
-            const uint16_t* Ks_next = lds + ((j + 1) & 1) * STAGE;
+        auto block = [&](int j, int kb, auto stage, f32x16 (&sc)[kQB], f32x16 (&sn)[kQB]) {
+            constexpr int ST = decltype(stage)::value;   // == j & 1
             const int bi = j * NKB + kb;
             const int kfirst = bi * 32;
             const bool live = bi < nb_live;            // wave-uniform
@@ -267,12 +301,12 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 for (int h = 0; h < 2; ++h)
     #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const uint16_t* vp = Vs + v_lane + (kb * 32 + 16 * h) * VSTR + db * 32;
+                        const char* vp = lds_b + v_off[db] + ST * STAGE_B + (kb * 32 + 16 * h) * RB;
                         const u32x2 lo = read_tr(vp);
-                        const u32x2 hi = read_tr(vp + 8 * VSTR);
+                        const u32x2 hi = read_tr(vp + 8 * RB);
                         va[h][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                     }
-                if (kb + 1 < NKB) read_k(ka, Ks, kb + 1);
+                if (kb + 1 < NKB) read_k(ka, ST, kb + 1);
                 // 2. statistics
                 const bool mask_blk = (CAUSAL && kfirst + 31 > q0w) || kfirst + 32 > N;
     #pragma unroll
@@ -309,10 +343,12 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             }
             // 3. tile boundary
             if (kb == NKB - 1) {
-                if (j + 1 < n_kv) store_tile((j + 1) & 1);
+                // tile j+1 (this wave's part) is in LDS; the barrier makes the whole tile
+                // visible and, with its wait on this wave's LDS reads, frees stage ST
+                wait_tile();
                 __syncthreads();
-                if (j + 2 < n_kv) load_tile(j + 2);
-                if (live) read_k(ka, Ks_next, 0);
+                if (j + 2 < n_kv) dma_tile(j + 2, ST);
+                if (live) read_k(ka, 1 - ST, 0);
             }
             // 4. next S^T, this block's weights and O^T update
             if (live) {
@@ -342,21 +378,28 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             }
         };
 
-        load_tile(0);
-        store_tile(0);
+        dma_tile(0, 0);
+        wait_tile();
         __syncthreads();
-        if (n_kv > 1) load_tile(1);
+        if (n_kv > 1) dma_tile(1, 1);
 
         static_assert(NKB == 2, "the block loop alternates two score buffers over two blocks per tile");
         f32x16 s_a[kQB], s_b[kQB];
         if (nb_live > 0) {
             u32x4 ka[NKS];
-            read_k(ka, lds, 0);
+            read_k(ka, 0, 0);
             s_product(ka, s_a);
         }
-        for (int j = 0; j < n_kv; ++j) {
-            block(j, 0, s_a, s_b);
-            block(j, 1, s_b, s_a);
+        // two tiles per trip, so that each block's LDS stage is a compile-time constant
+        using st0 = std::integral_constant<int, 0>;
+        using st1 = std::integral_constant<int, 1>;
+        for (int j = 0; j < n_kv; j += 2) {
+            block(j, 0, st0{}, s_a, s_b);
+            block(j, 1, st0{}, s_b, s_a);
+            if (j + 1 < n_kv) {
+                block(j + 1, 0, st1{}, s_a, s_b);
+                block(j + 1, 1, st1{}, s_b, s_a);
+            }
         }
 
         // a8: epilogue -- O = O~ / l, LSE = (m_ref + log2 l) ln 2
