@@ -85,13 +85,4 @@ __device__ inline u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<cons
 
 __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// Interleave the 16-bit halves of four dwords taken from four rows: returns the pair
-// (rows 0,1 of column lo/hi) and (rows 2,3 of column lo/hi) for a transposed write.
-__device__ inline u32x2 pack_col_lo(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3) {
-    return u32x2{(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
-}
-__device__ inline u32x2 pack_col_hi(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3) {
-    return u32x2{(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
-}
-
 }  // namespace attn

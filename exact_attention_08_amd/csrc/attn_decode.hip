@@ -18,15 +18,21 @@
 //     so faster workgroups take more items and the grid finishes together.  No workgroup is
 //     launched for a split past a sequence's context.
 //   * The G query heads are the columns of v_mfma_f32_16x16x32 (G <= 16), the 16 slots of
-//     a page its rows: S^T = K Q^T runs on the matrix cores with K loaded from HBM straight
-//     into the A operand.  The exponentiated scores of a page are exactly the B operand of
-//     O^T = V^T P^T on v_mfma_f32_16x16x16, so P stays in registers.
-//   * V is transposed through a small per-wave LDS slab (d-major); slots at or past the
-//     context length are written as zeros, so poisoned slots never reach the sum.
+//     a page its rows: S^T = K Q^T runs on the matrix cores.  The exponentiated scores of a
+//     page are exactly the B operand of O^T = V^T P^T on v_mfma_f32_16x16x16, so P stays in
+//     registers.
+//   * A page's K and V rows of one kv head are loaded a few whole 256-byte rows per
+//     instruction (a 64-byte piece of every row per instruction reaches far less of the HBM
+//     bandwidth), then staged through a per-wave LDS slab in XOR-swizzled rows: K is read
+//     back as the MFMA A operand, V^T with the transposing LDS read (ds_read_b64_tr_b16).
+//     V rows at or past the context length are written as zeros, so poisoned slots never
+//     reach the sum.
 //   * Each page is addressed through a buffer descriptor (page base in SGPRs, one VGPR of
 //     per-lane offset); block-table entries are scalar loads; K/V loads are non-temporal.
-//     Each wave keeps two pages in flight ahead of the one it computes, and the next
-//     item's first pages are loaded while the current one is merged.
+//     Two register sets per wave: a page's set is reloaded two pages ahead as soon as the
+//     page is in the slab, so two pages stay in flight while one is computed.  For
+//     1024-token splits the sweep is unrolled, so every wait on a load is counted exactly.
+//     The next item's first pages are loaded while the current one is merged.
 //   * The 8 waves of a workgroup take every 8th page of the item; their states are merged
 //     through LDS at the end of the item.  One workgroup per CU (rather than two of four
 //     waves) halves the time per item, so the queue's last items end closer together, and
@@ -44,6 +50,8 @@ constexpr int kPage = 16;
 constexpr int kLoadNT = 2;   // cache-policy operand of a buffer load: non-temporal
 constexpr int kDecWaves = 8;         // one workgroup per CU, two waves per SIMD
 constexpr int kDecThreads = 64 * kDecWaves;
+// A wave's pages per item up to which the page sweep is unrolled (1024-token splits)
+constexpr int kSweepUnroll = 8;
 
 // Work queues of the split kernel: per launch slot, [0] the next ticket and [1] the number
 // of workgroups that have finished.  The last workgroup of a launch to finish puts the slot
@@ -64,11 +72,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     using E = Elem<IS_BF16>;
     constexpr int NKS = D / 32;          // k-steps of S^T = K Q^T (32 dims each)
     constexpr int NDB = D / 16;          // 16-row d blocks of O^T
-    constexpr int VSTR = 16 + 8;         // LDS row stride of a wave's V^T slab (elements)
-    constexpr int KCH = D / 8;           // 16-byte chunks per K/V row
-    static_assert(4 * KCH <= 64, "a page's V must fit one 4-slot unit per lane");
-    constexpr int SLAB = D * VSTR;       // elements per wave slab
-    constexpr int LDS_BYTES_V = kDecWaves * SLAB * 2;
+    constexpr int RB = 2 * D;            // bytes per slot row
+    constexpr int CH = D / 8;            // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;         // slot rows per load instruction
+    constexpr int IPP = kPage / RPI;     // load instructions per page and tensor
+    constexpr int SLAB_B = 2 * kPage * RB;   // a wave's slab: the page's K rows, then its V rows
+    constexpr int LDS_BYTES_V = kDecWaves * SLAB_B;
     constexpr int LDS_BYTES_MERGE = kDecWaves * 16 * (D + 2) * 4;
     constexpr int LDS_BYTES = LDS_BYTES_V > LDS_BYTES_MERGE ? LDS_BYTES_V : LDS_BYTES_MERGE;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
@@ -86,15 +95,31 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     const int64_t row_stride = (int64_t)Hkv * D;   // elements between consecutive slots
     const int page_bytes = kPage * (int)row_stride * 2;
     const int slot_bytes = (int)row_stride * 2;
-    uint16_t* slab = reinterpret_cast<uint16_t*>(lds) + wave * SLAB;
+    unsigned char* slab = lds + wave * SLAB_B;
 
-    // per-lane offsets inside a page (bytes): K as the A operand (slot l16, dims 8*g4 +
-    // 32ks..), V as 4-slot units (slots 4*v_tg + e, dims 8*v_dc..+7; for d = 64 the upper
-    // half of the wave repeats the lower half)
-    const int vofs_k = (l16 * (int)row_stride + g4 * 8) * 2;
-    const int v_tg = lane & 3;
-    const int v_dc = (lane >> 2) & (KCH - 1);
-    const int vofs_v = (4 * v_tg * (int)row_stride + v_dc * 8) * 2;
+    // Loads: instruction i of a page reads slot rows RPI*i .. RPI*i + RPI-1 whole, lane l the
+    // 16-byte chunk l % CH of row RPI*i + l / CH (contiguous row pieces instead of a 64-byte
+    // piece of every row).  In the slab, chunk c of slot row r sits in slot c ^ swz(r) of the
+    // row; K is then read as the MFMA A operand (row l16, chunk 4ks + g4) and V^T with the
+    // transposing read, both touching every LDS bank once per pass.
+    auto k_swz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+    auto v_swz = [](int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+    const int ld_row = lane / CH, ld_ch = lane % CH;
+    const int vofs_ld = (ld_row * (int)row_stride + ld_ch * 8) * 2;   // + i * RPI rows
+    // slab byte offsets (K rows first, then V rows)
+    auto kw_off = [&](int i) { const int r = RPI * i + ld_row; return r * RB + 16 * (ld_ch ^ k_swz(r)); };
+    auto vw_off = [&](int i) {
+        const int r = RPI * i + ld_row;
+        return kPage * RB + r * RB + 16 * (ld_ch ^ v_swz(r));
+    };
+    auto kr_off = [&](int ks) { return l16 * RB + 16 * ((4 * ks + g4) ^ k_swz(l16)); };
+    // V^T operand (16x16x16 A: row d = 16 db + l16, slots 4 g4 + e): source lane 16G + 4e + a of
+    // the transposing read addresses slot row 4G + e, dims 16 db + 4a .. +3
+    const int vt_row = 4 * (lane >> 4) + ((lane >> 2) & 3);
+    const int vt_a = lane & 3;
+    auto vr_off = [&](int db) {
+        return kPage * RB + vt_row * RB + 16 * ((2 * db + (vt_a >> 1)) ^ v_swz(vt_row)) + 8 * (vt_a & 1);
+    };
 
     // Work list.  The non-empty splits are numbered t = 0 .. n_full + n_part - 1: first the
     // full splits (split_tokens tokens) of sequence 0, 1, ..., then the shorter last split of
@@ -242,7 +267,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
             qreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_vofs + ks * 64, 0, 0);
     };
 
-    struct Page { u32x4 k[NKS]; u32x4 v[4]; };
+    struct Page { u32x4 k[IPP]; u32x4 v[IPP]; };
     // Page i of this wave's share of item it.  Past the share (a prefetch beyond the last
     // page, or an invalid item) the descriptors have length 0: nothing is read and the
     // registers receive zeros.  The loads are issued either way, so the wait counter sees
@@ -260,18 +285,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
         // Every K/V byte is read exactly once: the loads are marked non-temporal (nt), so
         // they stream past the caches instead of displacing what is reused.
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            P.k[ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, vofs_k + ks * 64, 0, kLoadNT);
+        for (int i = 0; i < IPP; ++i)
+            P.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vofs_ld + i * RPI * slot_bytes, 0, kLoadNT);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            P.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, vofs_v + e * slot_bytes, 0, kLoadNT);
+        for (int i = 0; i < IPP; ++i)
+            P.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vofs_ld + i * RPI * slot_bytes, 0, kLoadNT);
     };
 
     if (tid == 0) s_ticket = (int)atomicAdd(&queue[0], 1u);
     __syncthreads();
     int f = s_ticket;
     Item it = setup(f);
-    Page b0, b1, b2;
+    Page b0, b1;
     load_q(it);
     load_page(it, b0, 0);
     load_page(it, b1, 1);
@@ -288,29 +313,36 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
 
-        auto compute_page = [&](const Page& P, int i) {
+        auto stage_page = [&](const Page& P, int i) {
+            const int t_pg = it.tok0 + (wave + kDecWaves * i) * kPage;   // first token of the page
+            const bool tail = t_pg + kPage > it.tok_end;                 // wave-uniform
+            // the page's K and V rows into the slab; V rows at or past the context are zeros, so
+            // poisoned slots never reach the sum
+#pragma unroll
+            for (int i = 0; i < IPP; ++i) {
+                const int r = RPI * i + ld_row;
+                const bool keep = !tail || t_pg + r < it.tok_end;
+                const u32x4 vz = keep ? P.v[i] : zero4();
+                *reinterpret_cast<u32x4*>(slab + kw_off(i)) = P.k[i];
+                *reinterpret_cast<u32x4*>(slab + vw_off(i)) = vz;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        auto math_page = [&](int i) {
             const int t_pg = it.tok0 + (wave + kDecWaves * i) * kPage;   // first token of the page
             const bool tail = t_pg + kPage > it.tok_end;                 // wave-uniform
             // S^T: rows = slots 4*g4 + v, column = head l16
             f32x4 s = f32x4{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) s = E::mfma16(P.k[ks], qreg[ks], s);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const u32x4 ka = *reinterpret_cast<const u32x4*>(slab + kr_off(ks));
+                s = E::mfma16(ka, qreg[ks], s);
+            }
             if (tail) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) s[v] = (t_pg + 4 * g4 + v < it.tok_end) ? s[v] : -INFINITY;
-            }
-            // V^T into the slab (zeros for slots past the context)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint32_t w[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = (!tail || t_pg + 4 * v_tg + e < it.tok_end) ? P.v[e][p] : 0u;
-                const int d = v_dc * 8 + 2 * p;
-                *reinterpret_cast<u32x2*>(&slab[d * VSTR + 4 * v_tg]) =
-                    pack_col_lo(w[0], w[1], w[2], w[3]);
-                *reinterpret_cast<u32x2*>(&slab[(d + 1) * VSTR + 4 * v_tg]) =
-                    pack_col_hi(w[0], w[1], w[2], w[3]);
             }
             // online softmax for the page (per head = per column l16)
             float mloc = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -329,14 +361,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
             }
             m_run = m_new;
             const u32x2 pb = {E::pack2(p[0], p[1]), E::pack2(p[2], p[3])};
-            // slab writes land before other lanes of the wave read them
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const u32x2 a = *reinterpret_cast<const u32x2*>(&slab[(db * 16 + l16) * VSTR + 4 * g4]);
-                oacc[db] = E::mfma16k16(a, pb, oacc[db]);
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(slab + vr_off(db)));
+                oacc[db] = E::mfma16k16(__builtin_bit_cast(u32x2, t), pb, oacc[db]);
             }
             // every lane has read the slab before the next page overwrites it
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -344,19 +374,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         };
 
-        // Page sweep: three register sets in rotation, two pages in flight ahead of the one
-        // being computed.
+        // Page sweep: two register sets; a page's set is reloaded (two pages ahead) as soon as
+        // the page is in the slab, so two pages are in flight while one is computed.
         const int cnt = it.cnt;
-        if (cnt > 0) {
+        if (cnt > 0 && cnt <= kSweepUnroll) {
+            // straight-line sweep (every wait on a load is counted exactly)
+#pragma unroll
+            for (int i = 0; i < kSweepUnroll; ++i) {
+                // the loads are issued on every path (empty past the item), so the wait counts
+                // below do not depend on cnt
+                Page& P = (i & 1) ? b1 : b0;
+                if (i < cnt) stage_page(P, i);
+                load_page(it, P, i + 2);
+                if (i < cnt) math_page(i);
+                __builtin_amdgcn_sched_barrier(0);   // keep pages apart (register pressure)
+            }
+        } else if (cnt > 0) {
             for (int i = 0;;) {
-                load_page(it, b2, i + 2);
-                compute_page(b0, i);
-                if (++i >= cnt) break;
+                stage_page(b0, i);
                 load_page(it, b0, i + 2);
-                compute_page(b1, i);
+                math_page(i);
                 if (++i >= cnt) break;
+                stage_page(b1, i);
                 load_page(it, b1, i + 2);
-                compute_page(b2, i);
+                math_page(i);
                 if (++i >= cnt) break;
             }
         }
