@@ -155,6 +155,18 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         if (slot >= n_slots) break;
         // the previous item's last LDS reads must be done before this item's first store
         if (round > 0) __syncthreads();
+        if (PERSIST) {
+            // Co-resident persistent workgroups keep their dispatch order for the whole
+            // kernel, and the instruction arbiter prefers the older waves, so the first
+            // workgroup on a CU would always run fastest.  A pseudo-random issue priority per
+            // item (three levels, from a hash of workgroup and round) spreads that advantage.
+            const unsigned h = (unsigned)(blockIdx.x * 2654435761u + round * 40503u);
+            switch ((h >> 16) % 3) {
+                case 0: __builtin_amdgcn_s_setprio(0); break;
+                case 1: __builtin_amdgcn_s_setprio(1); break;
+                default: __builtin_amdgcn_s_setprio(2); break;
+            }
+        }
         // Lane indices are rederived per item (the empty asm hides that they are loop
         // invariant): kept live across the item loop they would cost registers.
         int tid = threadIdx.x;
