@@ -51,6 +51,9 @@ def _bind(path: str):
     lib.oracle_decode_paged.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64,
                                         f64, i32, P, i64, P, P]
     lib.oracle_decode_paged.restype = i32
+    lib.oracle_decode_cascade.argtypes = [P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32,
+                                          i32, i64, f64, i32, P, i64, P, P]
+    lib.oracle_decode_cascade.restype = i32
     lib.oracle_online_row.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P]
     lib.oracle_online_row.restype = i32
     lib.oracle_merge.argtypes = [P, P, i32, i32, P, P]
@@ -150,6 +153,35 @@ def decode_paged(q, k_pages, v_pages, block_table, ctx_lens, scale: float, dtype
                                      _ptr(pr), n, _ptr(O), _ptr(L))
     if rc != 0:
         raise ValueError(f"oracle_decode_paged rejected its arguments ({rc})")
+    if pairs is None:
+        O, L = O.reshape(B, Hq, d), L.reshape(B, Hq)
+    return O, L
+
+
+def decode_cascade(q, k_prefix, v_prefix, k_pages, v_pages, block_table, ctx_lens,
+                   scale: float, dtype: int, pairs=None):
+    """Shared-prefix decode: every request attends to the shared prefix k/v_prefix
+    [Hkv, P, d] followed by its own paged tokens (as decode_paged).  Returns (O, LSE) like
+    decode_paged."""
+    q, kp, vp = _u16(q), _u16(k_pages), _u16(v_pages)
+    kpre, vpre = _u16(k_prefix), _u16(v_prefix)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    B, Hq, d = q.shape
+    num_pages, page, Hkv, d2 = kp.shape
+    Hkv2, P, d3 = kpre.shape
+    assert d2 == d and d3 == d and Hkv2 == Hkv and vpre.shape == kpre.shape
+    assert vp.shape == kp.shape and bt.shape[0] == B and ctx.shape == (B,)
+    pr = None if pairs is None else np.ascontiguousarray(pairs, dtype=np.int64)
+    n = B * Hq if pr is None else len(pr)
+    O = np.zeros((n, d), dtype=np.float64)
+    L = np.zeros(n, dtype=np.float64)
+    rc = _L().oracle_decode_cascade(_ptr(q), _ptr(kpre), _ptr(vpre), P, _ptr(kp), _ptr(vp),
+                                    _ptr(bt), _ptr(ctx), B, Hq, Hkv, d, page, bt.shape[1],
+                                    num_pages, float(scale), int(dtype), _ptr(pr), n, _ptr(O),
+                                    _ptr(L))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_cascade rejected its arguments ({rc})")
     if pairs is None:
         O, L = O.reshape(B, Hq, d), L.reshape(B, Hq)
     return O, L

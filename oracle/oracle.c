@@ -236,6 +236,80 @@ int oracle_decode_paged(const uint16_t* q, const uint16_t* Kp, const uint16_t* V
     return err;
 }
 
+/* ------------------------------------------------------------------ shared-prefix (cascade) decode
+ * [CS349D Lecture 4 notes, 4.4 and 5.3: requests that share a prefix attend to the prefix
+ * keys followed by their own keys; the cascade form is one way to compute the same result.]
+ * What is computed is its definition: for request r and query head h, standard attention of
+ * q[r,h] over the key sequence prefix (tokens 0..P-1 of Kpre/Vpre [Hkv, P, d], head h/G)
+ * followed by the request's own ctx_lens[r] tokens in the paged pool (as in
+ * oracle_decode_paged).  Same arguments as oracle_decode_paged plus the prefix.
+ * Returns 0, -1 on bad arguments, -2 if a needed table entry is outside [0, num_pages).     */
+int oracle_decode_cascade(const uint16_t* q, const uint16_t* Kpre, const uint16_t* Vpre,
+                          int prefix_len, const uint16_t* Kp, const uint16_t* Vp,
+                          const int32_t* block_table, const int32_t* ctx_lens, int B, int Hq,
+                          int Hkv, int d, int page_size, int max_pages, int64_t num_pages,
+                          double scale, int dtype, const int64_t* pairs, int64_t n_pairs,
+                          double* O, double* LSE)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || Hq % Hkv) return -1;
+    if (prefix_len < 0 || (prefix_len > 0 && (!Kpre || !Vpre))) return -1;
+    const int64_t total = (int64_t)B * Hq;
+    if (!pairs) n_pairs = total;
+    int max_ctx = 0;
+    for (int r = 0; r < B; ++r) {
+        if (ctx_lens[r] < 0 || ctx_lens[r] > (int64_t)max_pages * page_size) return -1;
+        if (ctx_lens[r] > max_ctx) max_ctx = ctx_lens[r];
+    }
+    const int group = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        int cap = prefix_len + max_ctx > 0 ? prefix_len + max_ctx : 1;
+        double* s = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* qq = (double*)malloc(sizeof(double) * (size_t)d);
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+        const uint16_t** kr = (const uint16_t**)malloc(sizeof(void*) * (size_t)cap);
+        const uint16_t** vr = (const uint16_t**)malloc(sizeof(void*) * (size_t)cap);
+        const int ok = s && qq && tmp && kr && vr;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n_pairs; ++t) {
+            int64_t p = pairs ? pairs[t] : t;
+            if (!ok || p < 0 || p >= total) {
+#pragma omp atomic write
+                err = -1;
+                continue;
+            }
+            int r = (int)(p / Hq), h = (int)(p % Hq), kvh = h / group;
+            int n = 0;
+            /* the shared prefix first ... */
+            for (int tok = 0; tok < prefix_len; ++tok, ++n) {
+                int64_t off = ((int64_t)kvh * prefix_len + tok) * d;   /* prefix head kvh */
+                kr[n] = Kpre + off;
+                vr[n] = Vpre + off;
+            }
+            /* ... then the request's own tokens */
+            int bad = 0;
+            for (int tok = 0; tok < ctx_lens[r]; ++tok, ++n) {
+                int32_t pg = block_table[(int64_t)r * max_pages + tok / page_size];
+                int in_page = tok % page_size;
+                if (pg < 0 || pg >= num_pages) { bad = 1; break; }
+                int64_t off = (((int64_t)pg * page_size + in_page) * Hkv + kvh) * d;
+                kr[n] = Kp + off;
+                vr[n] = Vp + off;
+            }
+            if (bad) {
+#pragma omp atomic write
+                err = -2;
+                continue;
+            }
+            widen_row(q + p * d, d, dtype, qq);
+            attend_row(qq, kr, vr, n, d, dtype, scale, s, tmp, O + t * d, LSE + t, NULL);
+        }
+        free(s); free(qq); free(tmp); free(kr); free(vr);
+    }
+    return err;
+}
+
 /* ------------------------------------------------------------------ online softmax, one row
  * s[n] scores (already scaled), v[n, dv] values, tiles of bc scores in order.
  * Outputs O[dv] = O~/l, *m_out, *l_out, *lse_out.  Optional trace arrays, one entry per tile

@@ -29,6 +29,11 @@ MUTANTS = {
     "fp16_wrong_bias": ("expo - 25);", "expo - 24);"),
     "online_l_not_rescaled": ("l = l * corr + rowsum;", "l = l + rowsum;"),
     "softmax_not_normalised": ("s[j] = s[j] / l;   /* P_ij */", "s[j] = s[j];"),
+    "cascade_prefix_other_head": ("int64_t off = ((int64_t)kvh * prefix_len + tok) * d;",
+                                  "int64_t off = ((int64_t)((kvh + 1) % Hkv) * prefix_len + tok) * d;"),
+    "cascade_drops_prefix": ("for (int tok = 0; tok < prefix_len; ++tok, ++n) {",
+                             "for (int tok = 0; tok < 0; ++tok, ++n) {"),
+    "cascade_own_tokens_wrong_slot": ("int in_page = tok % page_size;", "int in_page = (tok + 3) % page_size;"),
 }
 
 PINS = [
@@ -45,6 +50,7 @@ PINS = [
     lambda: pins.test_merge_is_order_free(8),
     pins.test_bsr_example_paged_equals_contiguous_exactly,
     pins.test_decode_matches_torch_sdpa_and_is_page_order_free,
+    pins.test_cascade_matches_torch_sdpa_over_prefix_then_own_tokens,
 ]
 
 

@@ -361,3 +361,61 @@ def test_decode_empty_context_reading():
     O, L = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
                                case.ctx_lens, case.scale, BF16)
     assert np.all(L[0] == -np.inf) and np.all(O[0] == 0.0) and np.all(np.isfinite(L[1]))
+
+
+# ----------------------------------------------------------------------------- shared prefix
+# [CS349D Lecture 4 notes, 4.4 and 5.3] requests that share a prefix attend to the prefix
+# keys followed by their own; the cascade split is one way to compute the same thing.
+
+def _prefix(Hkv, P, d, seed, dtype=BF16):
+    return (normal_bits((Hkv, P, d), seed, dtype), normal_bits((Hkv, P, d), seed + 1, dtype))
+
+
+def test_cascade_matches_torch_sdpa_over_prefix_then_own_tokens():
+    case = decode_case(4, 8, 2, 32, [0, 1, 37, 64], page_size=16, seeds=(71, 72, 73))
+    kpre, vpre = _prefix(2, 45, 32, 74)
+    O, L = oracle.decode_cascade(case.q, kpre, vpre, case.k_pages, case.v_pages,
+                                 case.block_table, case.ctx_lens, case.scale, BF16)
+    for r in range(case.B):
+        n = int(case.ctx_lens[r])
+        toks = np.arange(n)
+        pages = case.block_table[r, toks // 16]
+        own_k = bits_to_f64(case.k_pages[pages, toks % 16], BF16).transpose(1, 0, 2)
+        own_v = bits_to_f64(case.v_pages[pages, toks % 16], BF16).transpose(1, 0, 2)
+        kc = np.concatenate([bits_to_f64(kpre, BF16), own_k], axis=1)[None]
+        vc = np.concatenate([bits_to_f64(vpre, BF16), own_v], axis=1)[None]
+        qv = bits_to_f64(case.q[r], BF16)[None, :, None, :]
+        o = F.scaled_dot_product_attention(torch.from_numpy(qv), torch.from_numpy(kc),
+                                           torch.from_numpy(vc), scale=case.scale, enable_gqa=True)
+        np.testing.assert_allclose(O[r], o.numpy()[0, :, 0], rtol=1e-12, atol=1e-12)
+        s = case.scale * np.einsum("hd,hnd->hn", bits_to_f64(case.q[r], BF16),
+                                   np.repeat(kc[0], 4, axis=0))
+        np.testing.assert_allclose(L[r], sps.logsumexp(s, axis=-1), rtol=1e-12, atol=1e-12)
+
+
+def test_cascade_without_prefix_is_paged_decode():
+    case = decode_case(3, 4, 4, 16, [5, 0, 40], page_size=16, seeds=(75, 76, 77))
+    kpre = np.zeros((4, 0, 16), np.uint16)
+    O, L = oracle.decode_cascade(case.q, kpre, kpre, case.k_pages, case.v_pages,
+                                 case.block_table, case.ctx_lens, case.scale, BF16)
+    O2, L2 = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                 case.ctx_lens, case.scale, BF16)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_cascade_equals_merge_of_prefix_and_own_states():
+    case = decode_case(3, 6, 3, 16, [9, 1, 30], page_size=16, dtype=FP16, seeds=(78, 79, 80))
+    kpre, vpre = _prefix(3, 20, 16, 81, FP16)
+    O, L = oracle.decode_cascade(case.q, kpre, vpre, case.k_pages, case.v_pages,
+                                 case.block_table, case.ctx_lens, case.scale, FP16)
+    Oown, Lown = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                     case.ctx_lens, case.scale, FP16)
+    # the prefix alone: a request with no own tokens
+    nothing = np.zeros(case.B, np.int32)
+    Opre, Lpre = oracle.decode_cascade(case.q, kpre, vpre, case.k_pages, case.v_pages,
+                                       case.block_table, nothing, case.scale, FP16)
+    for r in range(case.B):
+        for h in range(case.Hq):
+            Om, Lm = oracle.merge(np.stack([Opre[r, h], Oown[r, h]]), np.array([Lpre[r, h], Lown[r, h]]))
+            np.testing.assert_allclose(O[r, h], Om, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(L[r, h], Lm, rtol=1e-12, atol=1e-12)
