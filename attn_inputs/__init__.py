@@ -204,3 +204,36 @@ def config_case(name: str):
     mp = (c["ctx_hi"] + c["page_size"] - 1) // c["page_size"]
     return decode_case(c["B"], c["Hq"], c["Hkv"], c["d"], ctx, c["page_size"], c["dtype"],
                        max_pages=mp)
+
+
+# ----------------------------------------------------------------------------- shared prefix
+SEED_PREFIX = 11    # prefix K; prefix V uses SEED_PREFIX + 1
+
+
+def cascade_case(B, Hq, Hkv, d, prefix_len, own_ctx, page_size=16, dtype=BF16, scale=None,
+                 seeds=(SEED_Q, SEED_K, SEED_V), prefix_seed=SEED_PREFIX, max_pages=None):
+    """Requests sharing one prefix: a decode case for the requests' own tokens, plus the
+    prefix K/V [Hkv, prefix_len, d] in case.extra["k_prefix"] / ["v_prefix"]."""
+    case = decode_case(B, Hq, Hkv, d, own_ctx, page_size, dtype, scale, seeds, max_pages=max_pages)
+    case.extra["k_prefix"] = normal_bits((Hkv, prefix_len, d), prefix_seed, dtype)
+    case.extra["v_prefix"] = normal_bits((Hkv, prefix_len, d), prefix_seed + 1, dtype)
+    return case
+
+
+# The shared-prefix workload: Llama-3-8B decode shapes, 64 requests forked from one
+# 8192-token prefix (a shared document or system prompt, the pages' motivating case), each
+# with its own log-uniform tail of 128-4096 tokens.
+CASCADE_WORKLOADS = {
+    "cascade_gqa_decode_b64_prefix8192_own128_4096": dict(
+        B=64, Hq=32, Hkv=8, d=128, page_size=16, prefix_len=8192, own_lo=128, own_hi=4096,
+        split_tokens=1024, dtype=BF16),
+}
+
+
+def cascade_workload(name: str):
+    c = CASCADE_WORKLOADS[name]
+    own = log_uniform_ctx(c["B"], c["own_lo"], c["own_hi"])
+    mp = (c["own_hi"] + c["page_size"] - 1) // c["page_size"]
+    return cascade_case(c["B"], c["Hq"], c["Hkv"], c["d"], c["prefix_len"], own,
+                        c["page_size"], c["dtype"], max_pages=mp)
+

@@ -9,6 +9,10 @@ missing the import fails, and a non-zero status from the library raises AttnErro
     attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_tokens,
                       workspace, scale=None, stream=None)
     attn_decode_paged_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq, split_tokens)
+    attn_decode_cascade(q, k_prefix, v_prefix, k_pages, v_pages, block_table, ctx_lens, O, LSE,
+                        split_tokens, workspace, scale=None, stream=None)
+    attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq, split_tokens,
+                                        prefix_len)
 """
 from __future__ import annotations
 
@@ -52,13 +56,19 @@ _lib.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _
 _lib.attn_decode_paged.restype = _i
 _lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.attn_decode_paged_workspace_bytes.restype = _sz
+_lib.attn_decode_cascade.argtypes = [_P, _P, _P, _i, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i,
+                                     _i, _i, _f, _i, _P, _sz, _P]
+_lib.attn_decode_cascade.restype = _i
+_lib.attn_decode_cascade_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+_lib.attn_decode_cascade_workspace_bytes.restype = _sz
 
 ATTN_OK = 0
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
           -4: "ATTN_ERR_UNSUPPORTED", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_WORKSPACE",
           -7: "ATTN_ERR_HIP"}
 ATTN_BF16, ATTN_FP16 = 0, 1
-EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_bytes")
+EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
+           "attn_decode_cascade", "attn_decode_cascade_workspace_bytes")
 
 
 class AttnError(RuntimeError):
@@ -156,3 +166,50 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_
                                   block_table.shape[1], int(split_tokens), float(scale), dt,
                                   workspace.data_ptr(), ws_bytes, _stream_ptr(q, stream))
     _check("attn_decode_paged", code)
+
+
+def attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq, split_tokens,
+                                        prefix_len) -> int:
+    return int(_lib.attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq,
+                                                        split_tokens, prefix_len))
+
+
+def attn_decode_cascade(q, k_prefix, v_prefix, k_pages, v_pages, block_table, ctx_lens, O, LSE,
+                        split_tokens: int, workspace, scale: float | None = None,
+                        stream=None) -> None:
+    """O (and LSE unless None) <- decode over the shared prefix k/v_prefix [Hkv, P, d]
+    followed by each request's own paged tokens (as attn_decode_paged)."""
+    import torch
+    for name, t in (("q", q), ("k_prefix", k_prefix), ("v_prefix", v_prefix),
+                    ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                    ("ctx_lens", ctx_lens), ("O", O), ("workspace", workspace)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(q.dim() == 3 and O.shape == q.shape, "q,O must be [B,Hq,d]")
+    B, Hq, d = q.shape
+    _need(k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "pages must be [P,page,Hkv,d]")
+    _, page, Hkv, d2 = k_pages.shape
+    _need(d2 == d, "page head dim must match q")
+    _need(k_prefix.dim() == 3 and v_prefix.shape == k_prefix.shape and k_prefix.shape[0] == Hkv
+          and k_prefix.shape[2] == d, "prefix must be [Hkv, P, d]")
+    P = k_prefix.shape[1]
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+          "block_table must be int32 [B,max_pages]")
+    _need(ctx_lens.dtype == torch.int32 and tuple(ctx_lens.shape) == (B,), "ctx_lens must be int32 [B]")
+    if LSE is not None:
+        _need(LSE.is_cuda and LSE.is_contiguous() and LSE.dtype == torch.float32 and
+              tuple(LSE.shape) == (B, Hq), "LSE must be fp32 [B,Hq]")
+    dt = _dtype_code(q)
+    _need(all(t.dtype == q.dtype for t in (k_pages, v_pages, k_prefix, v_prefix, O)),
+          "dtypes must match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    code = _lib.attn_decode_cascade(q.data_ptr(), k_prefix.data_ptr() if P else None,
+                                    v_prefix.data_ptr() if P else None, P, k_pages.data_ptr(),
+                                    v_pages.data_ptr(), block_table.data_ptr(),
+                                    ctx_lens.data_ptr(), O.data_ptr(),
+                                    None if LSE is None else LSE.data_ptr(), B, Hq, Hkv, d, page,
+                                    block_table.shape[1], int(split_tokens), float(scale), dt,
+                                    workspace.data_ptr(), ws_bytes, _stream_ptr(q, stream))
+    _check("attn_decode_cascade", code)
+

@@ -96,3 +96,54 @@ extern "C" int attn_decode_paged(const void* q, const void* Kpages, const void* 
                        workspace, stream};
     return attn::launch_decode(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
+
+extern "C" size_t attn_decode_cascade_workspace_bytes(int B, int Hq, int d, int page_size,
+                                                      int max_pages_per_seq, int split_tokens,
+                                                      int prefix_len) {
+    if (B <= 0 || Hq <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
+        split_tokens <= 0 || prefix_len < 0)
+        return 0;
+    const long long S = attn::decode_max_splits(page_size, max_pages_per_seq, split_tokens) +
+                        attn::cascade_chunks(prefix_len);
+    return attn::decode_workspace_bytes(B, Hq, d, S);
+}
+
+extern "C" int attn_decode_cascade(const void* q, const void* Kprefix, const void* Vprefix,
+                                   int prefix_len, const void* Kpages, const void* Vpages,
+                                   const int* block_table, const int* ctx_lens, void* O,
+                                   float* LSE, int B, int Hq, int Hkv, int d, int page_size,
+                                   int max_pages_per_seq, int split_tokens, float scale,
+                                   int dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    if (!q || !Kpages || !Vpages || !block_table || !ctx_lens || !O) return ATTN_ERR_NULL;
+    if (prefix_len < 0) return ATTN_ERR_SHAPE;
+    if (prefix_len > 0 && (!Kprefix || !Vprefix)) return ATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
+        split_tokens <= 0 || Hq % Hkv != 0)
+        return ATTN_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+    if (split_tokens % page_size != 0) return ATTN_ERR_UNSUPPORTED;
+    if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+    const long long S = attn::decode_max_splits(page_size, max_pages_per_seq, split_tokens) +
+                        attn::cascade_chunks(prefix_len);
+    if (S > 65535 || (long long)max_pages_per_seq * page_size > 0x7fffffffLL ||
+        (long long)B * Hq > 0x7fffffffLL || Hkv > 65535 || B > 65535)
+        return ATTN_ERR_SHAPE;
+    // q rows and one prefix head are addressed with 32-bit byte offsets
+    if ((long long)B * Hq * d * 2 > (1LL << 30) || (long long)prefix_len * d * 2 > (1LL << 30))
+        return ATTN_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(Kpages, 16) || !aligned(Vpages, 16) || !aligned(O, 16) ||
+        !aligned(block_table, 4) || !aligned(ctx_lens, 4) || (LSE && !aligned(LSE, 4)) ||
+        (prefix_len > 0 && (!aligned(Kprefix, 16) || !aligned(Vprefix, 16))))
+        return ATTN_ERR_ALIGN;
+    if (!workspace) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+    if (workspace_bytes < attn::decode_workspace_bytes(B, Hq, d, S)) return ATTN_ERR_WORKSPACE;
+    attn::DecodeArgs a{q, Kpages, Vpages, block_table, ctx_lens, O, LSE, B, Hq, Hkv, d,
+                       page_size, max_pages_per_seq, split_tokens, dtype == ATTN_BF16, scale,
+                       workspace, stream, Kprefix, Vprefix, prefix_len};
+    return attn::launch_decode(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}

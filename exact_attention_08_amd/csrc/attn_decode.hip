@@ -461,16 +461,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     }
 }
 
-// a13: fixed-order merge of the splits of one (sequence, head); one thread per dim.  The
-// loads are spread so that none waits for another: the split LSEs are read by all threads
-// at once (split s by thread s mod D) for the maximum, then the splits go in chunks of D,
-// thread d turning split c0 + d's LSE into its weight in LDS and every thread summing its
-// dim over the chunk in ascending split order with independent loads.
+// a13: fixed-order merge of the partial states of one (sequence, head); one thread per dim.
+// The states are the n_pre chunks of a shared prefix (at s_base.., cascade decode; none
+// otherwise) and then the sequence's splits, in key order.  The loads are spread so that
+// none waits for another: the LSEs are read by all threads at once (state u by thread
+// u mod D) for the maximum, then the states go in chunks of D, thread d turning state
+// c0 + d's LSE into its weight in LDS and every thread summing its dim over the chunk in
+// ascending order with independent loads.
 template <int D, bool IS_BF16>
 __global__ __launch_bounds__(D) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const int* __restrict__ ctx_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int Hq, int split_tokens, int S_max) {
+    int Hq, int split_tokens, int S_max, int n_pre, int s_base) {
     using E = Elem<IS_BF16>;
     constexpr int NW = D / 64;                 // waves per workgroup
     __shared__ float s_w[D];
@@ -479,12 +481,14 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
     const int r = rh / Hq;
     const int d = threadIdx.x;
     const int ctx = ctx_lens[r];
-    const int n_split = (ctx + split_tokens - 1) / split_tokens;
+    const int n_state = n_pre + (ctx + split_tokens - 1) / split_tokens;
     const float* lse_s = ws_lse + (int64_t)rh * S_max;
     const float* o_s = ws_o + (int64_t)rh * S_max * D;
+    // state u: prefix chunk u (u < n_pre), else split u - n_pre
+    auto slot = [&](int u) { return u < n_pre ? s_base + u : u - n_pre; };
 
     float M = -INFINITY;
-    for (int s = d; s < n_split; s += D) M = fmaxf(M, lse_s[s]);
+    for (int u = d; u < n_state; u += D) M = fmaxf(M, lse_s[slot(u)]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     if ((d & 63) == 0) s_red[d >> 6] = M;
@@ -494,36 +498,55 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
 
     const float log2e = 1.4426950408889634f;
     float wsum = 0.f, acc = 0.f;
-    for (int c0 = 0; c0 < n_split; c0 += D) {
-        const int s = c0 + d;
-        s_w[d] = s < n_split ? fast_exp2((lse_s[s] - M) * log2e) : 0.f;
+    for (int c0 = 0; c0 < n_state; c0 += D) {
+        const int u = c0 + d;
+        s_w[d] = u < n_state ? fast_exp2((lse_s[slot(u)] - M) * log2e) : 0.f;
         __syncthreads();
-        const int cnt = min(D, n_split - c0);
-        const float* oc = o_s + (int64_t)c0 * D + d;
+        const int cnt = min(D, n_state - c0);
+        if (n_pre == 0) {
+            const float* oc = o_s + (int64_t)c0 * D + d;
 #pragma unroll 8
-        for (int j = 0; j < cnt; ++j) {
-            const float w = s_w[j];
-            wsum += w;
-            acc += w * oc[(int64_t)j * D];
+            for (int j = 0; j < cnt; ++j) {
+                const float w = s_w[j];
+                wsum += w;
+                acc += w * oc[(int64_t)j * D];
+            }
+        } else {
+#pragma unroll 8
+            for (int j = 0; j < cnt; ++j) {
+                const float w = s_w[j];
+                wsum += w;
+                acc += w * o_s[(int64_t)slot(c0 + j) * D + d];
+            }
         }
         __syncthreads();
     }
-    const float out = (n_split > 0) ? acc / wsum : 0.f;
+    const float out = (n_state > 0) ? acc / wsum : 0.f;
     // store as 16 bits (RNE); pairs of threads cooperate through a packed write
     const float other = __shfl_xor(out, 1, 64);
     if ((d & 1) == 0)
         *reinterpret_cast<uint32_t*>(O + (int64_t)rh * D + d) = E::pack2(out, other);
-    if (LSE && d == 0) LSE[rh] = (n_split > 0) ? M + __logf(wsum) : -INFINITY;
+    if (LSE && d == 0) LSE[rh] = (n_state > 0) ? M + __logf(wsum) : -INFINITY;
 }
 
 template <int D, bool IS_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a) {
-    const long long S = decode_max_splits(a.page_size, a.max_pages, a.split_tokens);
+    // partial states per (sequence, head): the splits, then the prefix chunks (if any)
+    const long long S_split = decode_max_splits(a.page_size, a.max_pages, a.split_tokens);
+    const long long n_pre = a.prefix_len > 0 ? cascade_chunks(a.prefix_len) : 0;
+    const long long S = S_split + n_pre;
     float* ws_o = (float*)a.workspace;
     float* ws_lse = (float*)((char*)a.workspace + (size_t)a.B * a.Hq * (size_t)S * D * sizeof(float));
+    if (n_pre > 0) {
+        const CascadePrefixArgs pa{a.q, a.Kprefix, a.Vprefix, ws_o, ws_lse, a.B, a.Hq, a.Hkv, D,
+                                   a.prefix_len, kCascadeChunk, (int)n_pre, (int)S, (int)S_split,
+                                   a.is_bf16, a.scale, a.stream};
+        const hipError_t e = launch_cascade_prefix(pa);
+        if (e != hipSuccess) return e;
+    }
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     hipStream_t st = (hipStream_t)a.stream;
-    const long long max_items = (long long)a.B * S * a.Hkv;
+    const long long max_items = (long long)a.B * S_split * a.Hkv;
     const long long grid = std::min<long long>(max_items, (long long)device_cu_count());
     // each launch takes the next queue slot; concurrent launches (different streams) use
     // different slots as long as fewer than kDecSchedSlots are in flight on one device
@@ -538,7 +561,7 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     if (e != hipSuccess) return e;
     return launch_kernel(decode_merge_kernel<D, IS_BF16>, dim3((unsigned)(a.B * a.Hq)), dim3(D),
                          st, "decode_merge_kernel", ws_o, ws_lse, a.ctx_lens, a.O, a.LSE, a.Hq,
-                         a.split_tokens, (int)S);
+                         a.split_tokens, (int)S, (int)n_pre, (int)S_split);
 }
 
 }  // namespace

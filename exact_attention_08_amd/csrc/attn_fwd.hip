@@ -116,11 +116,28 @@ template <int D> __device__ __forceinline__ int v_swz(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST>
+// Shared-prefix (cascade) mode [CS349D Lecture 4 notes, 4.4 and 5.3]: the query rows of a
+// kv head are the single decode queries of all requests (request r, head kvh * G + g is row
+// r * G + g), so the prefix keys are read once for all of them; an item sweeps one chunk of
+// the prefix (non-causal) and writes its partial state -- O normalised, in fp32, and LSE --
+// among the split partials that the decode merge combines.
+struct CascadeGeo {
+    int n_rows;     // query rows per kv head (requests x G)
+    int chunk;      // prefix keys per item
+    int n_chunks;
+    int s_stride;   // partial states per (request, query head)
+    int s_base;     // index of the first prefix chunk among them
+};
+
+// CASC selects the shared-prefix mode: Q is the decode query q [B, Hq, d], K/V the prefix
+// [Hkv, N, d], O (as fp32) and LSE the partial-state buffers.
+template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST, bool CASC>
 __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int B, int Hq, int Hkv, int N, float scale_log2, int n_qtiles, int n_items, int xcd_major) {
+    int B, int Hq, int Hkv, int N, float scale_log2, int n_qtiles, int n_items, int xcd_major,
+    CascadeGeo cg) {
+    static_assert(!CASC || (!CAUSAL && !PERSIST), "the prefix mode is non-causal, one item per workgroup");
     using E = Elem<IS_BF16>;
     constexpr int BC = PrefillTile<D>::BC;
     constexpr int kQB = PrefillTile<D>::QB;
@@ -175,30 +192,59 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int l32 = lane & 31;
         const int g = lane >> 5;
-        const WorkItem wi = prefill_work_item(slot * P + x, n_qtiles, Hkv, G, xcd_major);
+        // prefix mode: item = (kv head, chunk, query tile), query tiles fastest so that the
+        // items sharing a chunk run together
+        const int chunk_id = CASC ? ((int)blockIdx.x / n_qtiles) % cg.n_chunks : 0;
+        const WorkItem wi = [&] {
+            if constexpr (CASC) {
+                WorkItem c;
+                c.qt = (int)blockIdx.x % n_qtiles;
+                c.kvh = (int)blockIdx.x / n_qtiles / cg.n_chunks;
+                c.b = 0;
+                c.h = 0;
+                return c;
+            } else {
+                return prefill_work_item(slot * P + x, n_qtiles, Hkv, G, xcd_major);
+            }
+        }();
         const int64_t qh_off = ((int64_t)wi.b * Hq + wi.h) * (int64_t)N;      // row offset of (b,h)
         const int64_t kh_off = ((int64_t)wi.b * Hkv + wi.kvh) * (int64_t)N;   // row offset of (b,kvh)
         const int head_bytes = N * D * 2;
-        const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + qh_off * D, head_bytes);
+        const int q_bytes = CASC ? B * Hq * D * 2 : head_bytes;
+        const __amdgpu_buffer_rsrc_t rq = head_rsrc(CASC ? Q : Q + qh_off * D, q_bytes);
 
         const int q_tile0 = wi.qt * kBR;
         const int q0w = q_tile0 + wave * (32 * kQB);   // first query row of this wave
-        const bool wave_live = q0w < N;
+        const int n_qrows = CASC ? cg.n_rows : N;
+        const bool wave_live = q0w < n_qrows;
 
-        // KV tiles this workgroup visits: causal stops after the block holding its last row.
-        const int kv_last = CAUSAL ? min(N, q_tile0 + kBR) - 1 : N - 1;
-        const int n_kv = kv_last / BC + 1;
-        const int wave_last_q = min(q0w + 32 * kQB - 1, N - 1);
+        // Keys of the item: [kbase, kend) (a prefix chunk, or the whole sequence).  KV tiles
+        // this workgroup visits: causal stops after the block holding its last row.
+        const int kbase = CASC ? chunk_id * cg.chunk : 0;
+        const int kend = CASC ? min(N, kbase + cg.chunk) : N;
+        const int kv_last = CAUSAL ? min(N, q_tile0 + kBR) - 1 : kend - 1;
+        const int n_kv = (kv_last - kbase) / BC + 1;
+        const int wave_last_q = min(q0w + 32 * kQB - 1, n_qrows - 1);
 
         // a2: this lane's Q rows (one per column block) as the B operand of S^T = K Q^T
-        // (k-values d = 16ks + 8g..+7); rows past N read as zero
+        // (k-values d = 16ks + 8g..+7); rows past the last query read as zero (offset past
+        // the buffer range)
+        auto q_offset = [&](int t, int ks) {
+            if constexpr (CASC) {
+                if (t >= cg.n_rows) return q_bytes;
+                const int rr = t / G;
+                return ((rr * Hq + wi.kvh * G + (t - rr * G)) * D + ks * 16 + g * 8) * 2;
+            } else {
+                return (t * D + ks * 16 + g * 8) * 2;
+            }
+        };
         u32x4 qreg[kQB][NKS];
     #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
     #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 qreg[qb][ks] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rq, ((q0w + 32 * qb + l32) * D + ks * 16 + g * 8) * 2, 0, 0);
+                    rq, q_offset(q0w + 32 * qb + l32, ks), 0, 0);
 
         // a3: K_j, V_j go from HBM straight into LDS stage st (buffer_load ... lds): wave load
         // i writes the 1 KiB block i * kWaves + wave of the tile, lane by lane in 16-byte
@@ -208,7 +254,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         const i32x4 rv4 = head_rsrc4(V + kh_off * D, head_bytes);
         const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)lds);
         auto dma_tile = [&](int j, int st) {
-            const int key0 = j * BC;
+            const int key0 = kbase + j * BC;
     #pragma unroll
             for (int i = 0; i < NDMA; ++i) {
                 const int blk = i * kWaves + wave;
@@ -302,7 +348,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         auto block = [&](int j, int kb, auto stage, f32x16 (&sc)[kQB], f32x16 (&sn)[kQB]) {
             constexpr int ST = decltype(stage)::value;   // == j & 1
             const int bi = j * NKB + kb;
-            const int kfirst = bi * 32;
+            const int kfirst = kbase + bi * 32;
             const bool live = bi < nb_live;            // wave-uniform
             u32x4 va[2][NDB];
             u32x4 ka[NKS];
@@ -320,7 +366,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                     }
                 if (kb + 1 < NKB) read_k(ka, ST, kb + 1);
                 // 2. statistics
-                const bool mask_blk = (CAUSAL && kfirst + 31 > q0w) || kfirst + 32 > N;
+                const bool mask_blk = (CAUSAL && kfirst + 31 > q0w) || kfirst + 32 > kend;
     #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
                     // a5: elementwise mask (select, never multiply)
@@ -329,7 +375,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     #pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const int key = kfirst + 8 * (v >> 2) + 4 * g + (v & 3);
-                            const bool masked = key >= N || (CAUSAL && key > q);
+                            const bool masked = key >= kend || (CAUSAL && key > q);
                             sc[qb][v] = masked ? -INFINITY : sc[qb][v];
                         }
                     }
@@ -418,9 +464,27 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
             const int q = q0w + 32 * qb + l32;
-            if (q >= N) continue;
+            if (q >= n_qrows) continue;
             const float l_tot = l_run[qb] + xor_lanes(l_run[qb], 32);
             const float inv_l = 1.f / l_tot;
+            if constexpr (CASC) {
+                // partial state of (request, head) for this chunk: O~/l in fp32, and LSE
+                const int rr = q / G;
+                const int64_t pidx = ((int64_t)rr * Hq + wi.kvh * G + (q - rr * G)) * cg.s_stride +
+                                     cg.s_base + chunk_id;
+                float* prow = reinterpret_cast<float*>(O) + pidx * D;
+    #pragma unroll
+                for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const f32x16& o = oacc[qb][db];
+                        *reinterpret_cast<f32x4*>(prow + db * 32 + 8 * a + 4 * g) =
+                            f32x4{o[4 * a + 0] * inv_l, o[4 * a + 1] * inv_l, o[4 * a + 2] * inv_l,
+                                  o[4 * a + 3] * inv_l};
+                    }
+                if (g == 0) LSE[pidx] = (m_ref[qb] + fast_log2(l_tot)) * kLn2;
+                continue;
+            }
             uint16_t* orow = O + (qh_off + q) * D;
     #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -456,14 +520,29 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     const long long grid = persistent && n_items > slots ? slots : n_items;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     if (grid < n_items)
-        return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, true>, dim3((unsigned)grid),
-                             dim3(kThreads), (hipStream_t)a.stream, "prefill_fwd_kernel", a.Q,
-                             a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N, scale_log2, n_qtiles,
-                             (int)n_items, xcd_major);
-    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false>, dim3((unsigned)grid),
-                         dim3(kThreads), (hipStream_t)a.stream, "prefill_fwd_kernel", a.Q, a.K,
-                         a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N, scale_log2, n_qtiles,
-                         (int)n_items, xcd_major);
+        return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, true, false>,
+                             dim3((unsigned)grid), dim3(kThreads), (hipStream_t)a.stream,
+                             "prefill_fwd_kernel", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv,
+                             a.N, scale_log2, n_qtiles, (int)n_items, xcd_major, CascadeGeo{});
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, false>,
+                         dim3((unsigned)grid), dim3(kThreads), (hipStream_t)a.stream,
+                         "prefill_fwd_kernel", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N,
+                         scale_log2, n_qtiles, (int)n_items, xcd_major, CascadeGeo{});
+}
+
+template <int D, bool IS_BF16>
+hipError_t launch_cascade_prefix_t(const CascadePrefixArgs& a) {
+    constexpr int kBR = 32 * PrefillTile<D>::QB * kWaves;
+    const int n_rows = a.B * (a.Hq / a.Hkv);
+    const int n_qtiles = (n_rows + kBR - 1) / kBR;
+    const long long n_items = (long long)n_qtiles * a.Hkv * a.n_chunks;
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    const CascadeGeo cg{n_rows, a.chunk, a.n_chunks, a.s_stride, a.s_base};
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, false, false, true>,
+                         dim3((unsigned)n_items), dim3(kThreads), (hipStream_t)a.stream,
+                         "prefill_fwd_kernel(prefix)", a.q, a.Kprefix, a.Vprefix,
+                         reinterpret_cast<uint16_t*>(a.ws_o), a.ws_lse, a.B, a.Hq, a.Hkv,
+                         a.prefix_len, scale_log2, n_qtiles, (int)n_items, 0, cg);
 }
 
 }  // namespace
@@ -478,6 +557,12 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.is_bf16) return a.causal ? launch_prefill_t<64, true, true>(a)
                                    : launch_prefill_t<64, true, false>(a);
     return a.causal ? launch_prefill_t<64, false, true>(a) : launch_prefill_t<64, false, false>(a);
+}
+
+hipError_t launch_cascade_prefix(const CascadePrefixArgs& a) {
+    if (a.d == 128) return a.is_bf16 ? launch_cascade_prefix_t<128, true>(a)
+                                     : launch_cascade_prefix_t<128, false>(a);
+    return a.is_bf16 ? launch_cascade_prefix_t<64, true>(a) : launch_cascade_prefix_t<64, false>(a);
 }
 
 }  // namespace attn

@@ -32,6 +32,25 @@ struct DecodeArgs {
     float scale;
     void* workspace;
     void* stream;
+    // shared prefix (cascade decode): K/V [Hkv, prefix_len, d]; prefix_len 0 = none
+    const void* Kprefix = nullptr;
+    const void* Vprefix = nullptr;
+    int prefix_len = 0;
+};
+
+// The prefix part of a cascade decode: partial states of every (request, query head) for
+// each chunk of the shared prefix, written at split index s_base + chunk of the partial
+// buffers (s_stride states per pair).
+struct CascadePrefixArgs {
+    const void* q;
+    const void* Kprefix;
+    const void* Vprefix;
+    float* ws_o;
+    float* ws_lse;
+    int B, Hq, Hkv, d, prefix_len, chunk, n_chunks, s_stride, s_base;
+    bool is_bf16;
+    float scale;
+    void* stream;
 };
 
 // Launch through hipLaunchKernel so the status reflects this launch only (a sticky error
@@ -61,6 +80,13 @@ int device_cu_count();
 
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_cascade_prefix(const CascadePrefixArgs& a);
+
+// Prefix keys per partial state in a cascade decode.
+constexpr int kCascadeChunk = 1024;
+inline long long cascade_chunks(int prefix_len) {
+    return ((long long)prefix_len + kCascadeChunk - 1) / kCascadeChunk;
+}
 
 // Number of splits per sequence the workspace is sized for.
 inline long long decode_max_splits(int page_size, int max_pages, int split_tokens) {

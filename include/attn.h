@@ -1,7 +1,8 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
  *
- * Two compute calls follow the problem statement of the pages:
+ * Two compute calls follow the problem statement of the pages (a third serves requests that
+ * share a prefix):
  *   attn_fwd           exact scaled-dot-product attention forward (prefill), computed as a
  *                      tiled, fused kernel with online softmax: Q row-blocks stay on chip
  *                      while K/V column-blocks stream past, fully masked causal blocks are
@@ -15,6 +16,9 @@
  *                      [CS349D Lecture 4 notes 4.2-4.3; LLM Internals 10.3.7; AI-infra
  *                      handbook "FlashAttention and inference operators", Flash-Decoding
  *                      split-K merge and the paged GQA decode kernel]
+ *   attn_decode_cascade  decode for requests that share a prefix: the prefix is read once for
+ *                      all of them, then merged with each request's own tokens by the LSE
+ *                      rule [CS349D Lecture 4 notes 4.4, 5.3]
  *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
@@ -126,6 +130,44 @@ int attn_decode_paged(const void* q, const void* Kpages, const void* Vpages,
  */
 size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int page_size,
                                          int max_pages_per_seq, int split_tokens);
+
+/*
+ * attn_decode_cascade -- shared-prefix (cascade) decode [CS349D Lecture 4 notes, 4.4 and
+ * 5.3]: every request r attends to the same prefix of prefix_len tokens followed by its own
+ * ctx_lens[r] tokens in the paged pool; the result is standard attention over that key
+ * sequence, computed as (a) the queries of all requests against the prefix, which is read
+ * once, as matrix-matrix products in chunks of prefix keys, (b) each request's own tokens as
+ * in attn_decode_paged, and (c) one merge of all partial states with the LSE rule in key
+ * order (prefix chunks, then splits).
+ *
+ *   q          [B, Hq, d]               the query of each request, one token
+ *   Kprefix,   [Hkv, prefix_len, d]     the shared prefix, head-major (as attn_fwd takes K
+ *   Vprefix                              and V for one sequence); may be NULL if prefix_len
+ *                                        is 0
+ *   prefix_len >= 0 tokens; 0 makes the call equal to attn_decode_paged
+ *   Kpages, Vpages, block_table, ctx_lens, O, LSE, sizes, split_tokens, scale, dtype,
+ *   workspace, stream: as in attn_decode_paged (ctx_lens counts only a request's own
+ *   tokens).  A request with no keys at all gets O = 0 and LSE = -inf.
+ *   workspace  at least attn_decode_cascade_workspace_bytes(...) bytes
+ *
+ *   Supported: as attn_decode_paged; also B * Hq * d * 2 and prefix_len * d * 2 must not
+ *   exceed 2^30 (32-bit addressing of q and of one prefix head).  Returns ATTN_OK or a
+ *   negative attn_status.
+ */
+int attn_decode_cascade(const void* q, const void* Kprefix, const void* Vprefix, int prefix_len,
+                        const void* Kpages, const void* Vpages, const int* block_table,
+                        const int* ctx_lens, void* O, float* LSE, int B, int Hq, int Hkv, int d,
+                        int page_size, int max_pages_per_seq, int split_tokens, float scale,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_cascade_workspace_bytes -- host-only helper: the workspace attn_decode_cascade
+ * needs (the partial states of every split and every prefix chunk of every (request, head)).
+ * Returns 0 when the sizes are invalid.  Makes no HIP call.
+ */
+size_t attn_decode_cascade_workspace_bytes(int B, int Hq, int d, int page_size,
+                                           int max_pages_per_seq, int split_tokens,
+                                           int prefix_len);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ def declared_functions():
     return sorted(set(re.findall(r"^(?:int|size_t)\s+(attn_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_two_calls_and_the_helper():
+def test_header_declares_the_calls_and_the_helpers():
     assert declared_functions() == sorted(attn.EXPORTS)
 
 
@@ -99,3 +99,41 @@ def test_workspace_helper():
     assert ws(64, 32, 128, 16, 2048, 1024) == o + ((l + 255) // 256) * 256
     assert ws(0, 32, 128, 16, 2048, 1024) == 0
     assert ws(1, 1, 64, 16, 1, 16) >= 64 * 4 + 4
+
+
+def casc(q=A, Kp=A, Vp=A, P=100, K=A, V=A, bt=A, ctx=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, d=128,
+         page=16, max_pages=8, split=64, scale=0.1, dtype=0, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.attn_decode_cascade_workspace_bytes(B, Hq, d, 16, max_pages, max(split, 16),
+                                                         max(P, 0))
+    return L.attn_decode_cascade(q, Kp, Vp, P, K, V, bt, ctx, O, LSE, B, Hq, Hkv, d, page,
+                                 max_pages, split, scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(K=None), -1), (dict(bt=None), -1), (dict(O=None), -1),
+    (dict(Kp=None), -1), (dict(Vp=None), -1),
+    (dict(P=-1), -2), (dict(B=0), -2), (dict(Hq=7), -2), (dict(split=0), -2),
+    (dict(scale=0.0), -2), (dict(P=(1 << 22) + 1), -2),
+    (dict(dtype=5), -3),
+    (dict(d=80), -4), (dict(page=32), -4), (dict(split=24), -4), (dict(Hq=64, Hkv=2), -4),
+    (dict(q=MIS), -5), (dict(Kp=MIS), -5), (dict(Vp=MIS), -5), (dict(O=MIS), -5),
+    (dict(ws=MIS), -5),
+    (dict(ws=None), -6), (dict(ws_bytes=100), -6),
+])
+def test_attn_decode_cascade_rejects_bad_arguments(kw, code):
+    assert casc(**kw) == code
+
+
+def test_cascade_workspace_helper_adds_the_prefix_chunks():
+    paged = L.attn_decode_paged_workspace_bytes
+    cw = L.attn_decode_cascade_workspace_bytes
+    # no prefix: the same workspace as the paged call
+    assert cw(64, 32, 128, 16, 2048, 1024, 0) == paged(64, 32, 128, 16, 2048, 1024)
+    # a prefix of 4097 tokens adds 5 partial states (chunks of 1024 keys) per (request, head)
+    S = (2048 * 16 + 1023) // 1024 + 5
+    o = 64 * 32 * S * 128 * 4
+    l = 64 * 32 * S * 4
+    assert cw(64, 32, 128, 16, 2048, 1024, 4097) == o + ((l + 255) // 256) * 256
+    assert cw(64, 32, 128, 16, 2048, 1024, -1) == 0
+
