@@ -13,7 +13,9 @@ Printed: one JSON line.  `value` is the prefill throughput in TFLOP/s (algorithm
 4*B*H*N^2*d/2 for causal); the decode half of the metric is in `decode` (algorithmic bytes:
 every K/V element of every context read once, plus q, O, block table and lengths).
 `roofline` covers the prefill kernel, `decode.roofline` the decode call; `cpu_baseline`
-times the fp64 CPU oracle on a bounded sample of the same workloads.
+times the fp64 CPU oracle on a bounded sample of the same workloads.  Outside the step
+(skipped with --no-extra): the Llama-3-8B prefill shapes, and the shared-prefix decode
+(attn_decode_cascade) next to the same requests through attn_decode_paged.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--cpu-seconds 10] [--no-extra]
 """
@@ -35,6 +37,7 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 PREFILL = "gpt2_medium_b64_h16_n1024_d64_causal"
 DECODE = "paged_gqa_decode_b64_ctx512_32768"
 EXTRA = ["llama3_8b_prefill_n8192_causal", "llama3_8b_prefill_n32768_causal"]
+CASCADE = "cascade_gqa_decode_b64_prefix8192_own128_4096"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -61,6 +64,84 @@ def decode_bytes(c):
 
 def decode_flops(c):
     return 4.0 * c.Hq * c.d * float(c.ctx_lens.astype("int64").sum())
+
+
+def cascade_bytes(c, prefix_len):
+    """Algorithmic bytes of a shared-prefix decode: the prefix K/V once, every request's own
+    K/V once, q read, O written, table entries, lengths and LSE."""
+    own, _ = decode_bytes(c)
+    return own + prefix_len * c.Hkv * c.d * 2 * 2
+
+
+def cascade_figure(attn, torch, dev, log):
+    """Shared-prefix decode (CASCADE workload) against the same requests through the plain
+    paged decode, whose block tables all point at one shared copy of the prefix pages (what
+    a paged cache with prefix sharing holds).  Returns a dict for the JSON line."""
+    import numpy as np
+    from attn_inputs import CASCADE_WORKLOADS, cascade_workload
+    cw = CASCADE_WORKLOADS[CASCADE]
+    log(f"bench: extra figure {CASCADE}")
+    c = cascade_workload(CASCADE)
+    P, split, page = cw["prefix_len"], cw["split_tokens"], c.page_size
+    assert P % page == 0, "the plain layout below starts each request's own tokens on a page"
+    q = to_dev(c.q, c.dtype)
+    kpre, vpre = to_dev(c.extra["k_prefix"], c.dtype), to_dev(c.extra["v_prefix"], c.dtype)
+    kp, vp = to_dev(c.k_pages, c.dtype), to_dev(c.v_pages, c.dtype)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    ctx = torch.from_numpy(c.ctx_lens).to(dev)
+    O = torch.empty_like(q)
+    L = torch.empty(c.B, c.Hq, dtype=torch.float32, device=dev)
+    ws = torch.empty(attn.attn_decode_cascade_workspace_bytes(c.B, c.Hq, c.d, page, c.max_pages,
+                                                              split, P),
+                     dtype=torch.uint8, device=dev)
+    # the plain layout: prefix pages first in the pool, shared by every request's table
+    npre = (P + page - 1) // page
+    kpre_pages = kpre.permute(1, 0, 2).reshape(npre, page, c.Hkv, c.d)
+    vpre_pages = vpre.permute(1, 0, 2).reshape(npre, page, c.Hkv, c.d)
+    kp_all = torch.cat([kpre_pages, kp]).contiguous()
+    vp_all = torch.cat([vpre_pages, vp]).contiguous()
+    own_t = torch.from_numpy(c.block_table.astype(np.int64))
+    bt_all = torch.full((c.B, npre + c.max_pages), -1, dtype=torch.int64)
+    bt_all[:, :npre] = torch.arange(npre)
+    bt_all[:, npre:] = torch.where(own_t >= 0, own_t + npre, own_t)
+    bt_all = bt_all.to(torch.int32).to(dev)
+    ctx_all = ctx + P
+    O2 = torch.empty_like(q)
+    L2 = torch.empty_like(L)
+    ws2 = torch.empty(attn.attn_decode_paged_workspace_bytes(c.B, c.Hq, c.d, page, npre + c.max_pages,
+                                                             split), dtype=torch.uint8, device=dev)
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t_c = timed(lambda: attn.attn_decode_cascade(q, kpre, vpre, kp, vp, bt, ctx, O, L, split, ws,
+                                                 c.scale))
+    t_p = timed(lambda: attn.attn_decode_paged(q, kp_all, vp_all, bt_all, ctx_all, O2, L2, split,
+                                               ws2, c.scale))
+    diff = float((O.float() - O2.float()).abs().max())
+    assert diff < 0.05 and torch.isfinite(L).all(), f"cascade and plain decode disagree ({diff})"
+    b = cascade_bytes(c, P)
+    gbs = b / t_c / 1e9
+    out = {"workload": CASCADE, "avg_call_us": round(t_c * 1e6, 1),
+           "algorithmic_bytes_per_call": b, "gbs": round(gbs, 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "kernel": "prefill_fwd_kernel(prefix chunks) + decode_split_kernel + "
+                                  "decode_merge_kernel"},
+           "plain_paged_decode_us": round(t_p * 1e6, 1),
+           "speedup_vs_plain": round(t_p / t_c, 2),
+           "max_abs_diff_vs_plain": diff}
+    del q, kpre, vpre, kp, vp, kp_all, vp_all, ws, ws2
+    torch.cuda.empty_cache()
+    return out
 
 
 def source_digest(files):
@@ -284,6 +365,10 @@ def main():
             del Qx, Kx, Vx, Ox, Lx
             torch.cuda.empty_cache()
 
+    casc = None
+    if not args.no_extra and args.only is None:
+        casc = cascade_figure(attn, torch, dev, log)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
@@ -313,6 +398,7 @@ def main():
             "tflops": round(decode_flops(dc) / t_dec / 1e12, 2),
             "roofline": roof_dec},
         "extra_prefill": extra or None,
+        "cascade_decode": casc,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

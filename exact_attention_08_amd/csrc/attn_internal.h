@@ -83,7 +83,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_cascade_prefix(const CascadePrefixArgs& a);
 
 // Prefix keys per partial state in a cascade decode.
-constexpr int kCascadeChunk = 1024;
+constexpr int kCascadeChunk = 512;
 inline long long cascade_chunks(int prefix_len) {
     return ((long long)prefix_len + kCascadeChunk - 1) / kCascadeChunk;
 }

@@ -130,8 +130,8 @@ def test_cascade_workspace_helper_adds_the_prefix_chunks():
     cw = L.attn_decode_cascade_workspace_bytes
     # no prefix: the same workspace as the paged call
     assert cw(64, 32, 128, 16, 2048, 1024, 0) == paged(64, 32, 128, 16, 2048, 1024)
-    # a prefix of 4097 tokens adds 5 partial states (chunks of 1024 keys) per (request, head)
-    S = (2048 * 16 + 1023) // 1024 + 5
+    # a prefix of 4097 tokens adds 9 partial states (chunks of 512 keys) per (request, head)
+    S = (2048 * 16 + 1023) // 1024 + 9
     o = 64 * 32 * S * 128 * 4
     l = 64 * 32 * S * 4
     assert cw(64, 32, 128, 16, 2048, 1024, 4097) == o + ((l + 255) // 256) * 256
