@@ -231,9 +231,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the Llama-3-8B prefill figures")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="(profiling) run only one half of the step")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the Llama-3-8B prefill figures and the shared-prefix decode figure")
+    ap.add_argument("--only", choices=["prefill", "decode", "cascade"], default=None,
+                    help="(profiling) run only one half of the step, or only the shared-prefix "
+                         "decode figure")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -251,6 +253,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
+
+    if args.only == "cascade":
+        print(json.dumps({"cascade_decode": cascade_figure(attn, torch, dev, log)}), flush=True)
+        return
 
     log("bench: generating inputs")
     pc = config_case(PREFILL)
