@@ -237,3 +237,84 @@ def cascade_workload(name: str):
     return cascade_case(c["B"], c["Hq"], c["Hkv"], c["d"], c["prefix_len"], own,
                         c["page_size"], c["dtype"], max_pages=mp)
 
+
+
+# ----------------------------------------------------------------------------- paged / varlen prefill
+@dataclass
+class PagedPrefillCase:
+    Hq: int
+    Hkv: int
+    d: int
+    page_size: int
+    dtype: int
+    scale: float
+    causal: bool
+    q_lens: np.ndarray       # int32 [B] new tokens per request
+    kv_lens: np.ndarray      # int32 [B] cached tokens per request, the new ones included
+    cu_seqlens_q: np.ndarray  # int32 [B + 1]
+    block_table: np.ndarray  # int32 [B, max_pages]
+    num_pages: int
+    q: np.ndarray            # uint16 [total_q, Hq, d]
+    k_pages: np.ndarray      # uint16 [num_pages, page, Hkv, d]
+    v_pages: np.ndarray
+
+    @property
+    def B(self) -> int:
+        return len(self.kv_lens)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return self.block_table.shape[1]
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_lens.max()) if len(self.q_lens) else 0
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """Packed-sequence offsets [0, l0, l0+l1, ...] (int32, length B + 1)."""
+    out = np.zeros(len(lengths) + 1, dtype=np.int32)
+    out[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return out
+
+
+def paged_prefill_case(Hq, Hkv, d, q_lens, kv_lens, page_size=16, dtype=BF16, causal=True,
+                       scale=None, seeds=(SEED_Q, SEED_K, SEED_V), perm_seed=SEED_PERM,
+                       max_pages=None, pad_q=0) -> PagedPrefillCase:
+    """New queries of several requests packed end to end ([total_q, Hq, d], total_q =
+    sum(q_lens) + pad_q padding rows), over paged caches of kv_lens tokens each."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    kv_lens = np.asarray(kv_lens, dtype=np.int32)
+    table, total = paged_layout(kv_lens, page_size, perm_seed, max_pages)
+    cu = cu_seqlens(q_lens)
+    q = normal_bits((int(cu[-1]) + pad_q, Hq, d), seeds[0], dtype)
+    kp = normal_bits((max(total, 1), page_size, Hkv, d), seeds[1], dtype)
+    vp = normal_bits((max(total, 1), page_size, Hkv, d), seeds[2], dtype)
+    return PagedPrefillCase(Hq, Hkv, d, page_size, dtype, float(scale), bool(causal), q_lens,
+                            kv_lens, cu, table, total, q, kp, vp)
+
+
+SEED_QLEN = 6
+
+# Chunked prefill at Llama-3-8B shapes: 16 requests, each appending a chunk of new tokens
+# (log-uniform 256-2048, seed 6) to a cached history (log-uniform 1024-16384 tokens, seed 5),
+# the situation of incremental prefill and multi-turn chat on the pages.
+PAGED_PREFILL_WORKLOADS = {
+    "chunked_prefill_b16_hist1024_16384_chunk256_2048": dict(
+        B=16, Hq=32, Hkv=8, d=128, page_size=16, hist_lo=1024, hist_hi=16384, q_lo=256,
+        q_hi=2048, dtype=BF16),
+}
+
+
+def paged_prefill_workload(name: str) -> PagedPrefillCase:
+    c = PAGED_PREFILL_WORKLOADS[name]
+    hist = log_uniform_ctx(c["B"], c["hist_lo"], c["hist_hi"])
+    qn = log_uniform_ctx(c["B"], c["q_lo"], c["q_hi"], seed=SEED_QLEN)
+    return paged_prefill_case(c["Hq"], c["Hkv"], c["d"], qn, hist + qn, c["page_size"],
+                              c["dtype"])

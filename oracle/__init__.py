@@ -54,6 +54,9 @@ def _bind(path: str):
     lib.oracle_decode_cascade.argtypes = [P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32,
                                           i32, i64, f64, i32, P, i64, P, P]
     lib.oracle_decode_cascade.restype = i32
+    lib.oracle_prefill_paged.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64,
+                                         i32, i32, f64, i32, P, i64, P, P]
+    lib.oracle_prefill_paged.restype = i32
     lib.oracle_online_row.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P]
     lib.oracle_online_row.restype = i32
     lib.oracle_merge.argtypes = [P, P, i32, i32, P, P]
@@ -184,6 +187,34 @@ def decode_cascade(q, k_prefix, v_prefix, k_pages, v_pages, block_table, ctx_len
         raise ValueError(f"oracle_decode_cascade rejected its arguments ({rc})")
     if pairs is None:
         O, L = O.reshape(B, Hq, d), L.reshape(B, Hq)
+    return O, L
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens, causal: bool,
+                  scale: float, dtype: int, rows=None):
+    """Paged / varlen prefill: q [total_q, Hq, d] packed by cu_seqlens_q [B+1]; each request's
+    cache (pools [P,page,Hkv,d], table [B,max_pages]) holds kv_lens[r] tokens, its new ones
+    last.  rows: optional flat (token*Hq + h).  Returns (O [total_q,Hq,d] or [n,d], LSE)."""
+    q, kp, vp = _u16(q), _u16(k_pages), _u16(v_pages)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    kvl = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    total_q, Hq, d = q.shape
+    num_pages, page, Hkv, d2 = kp.shape
+    B = kvl.shape[0]
+    assert d2 == d and vp.shape == kp.shape and bt.shape[0] == B and cu.shape == (B + 1,)
+    pr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = total_q * Hq if pr is None else len(pr)
+    O = np.zeros((n, d), dtype=np.float64)
+    L = np.zeros(n, dtype=np.float64)
+    rc = _L().oracle_prefill_paged(_ptr(q), _ptr(kp), _ptr(vp), _ptr(bt), _ptr(cu), _ptr(kvl),
+                                   B, Hq, Hkv, d, page, bt.shape[1], num_pages, total_q,
+                                   int(bool(causal)), float(scale), int(dtype), _ptr(pr), n,
+                                   _ptr(O), _ptr(L))
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_paged rejected its arguments ({rc})")
+    if rows is None:
+        O, L = O.reshape(total_q, Hq, d), L.reshape(total_q, Hq)
     return O, L
 
 

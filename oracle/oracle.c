@@ -21,6 +21,15 @@
  *                        lives in physical page block_table[r][t / page] at slot t % page
  *                        [handbook, PagedAttention section; LLM Internals 10.3.7].  All ctx
  *                        tokens are visible.  The row itself is the same standard attention.
+ *   oracle_prefill_paged A chunk of new queries per request over its paged KV cache: the
+ *                        requests' queries are packed end to end, request r owning rows
+ *                        cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 [LLM Internals 10.3.8,
+ *                        variable-length batching]; its cache holds kv_lens[r] tokens, the
+ *                        last q_len of them being the new tokens themselves [LLM Internals
+ *                        10.3.7; CS349D Lecture 4 section 5.1, incremental prefill].  Causal:
+ *                        new query i sits at position kv_len - q_len + i and sees the keys at
+ *                        positions up to its own, so q_len = 1 is a decode step and
+ *                        q_len = kv_len is ordinary causal prefill.
  *   oracle_online_row    FlashAttention-2 loop order for one row: tiles of Bc scores, running
  *                        max m, exp-sum l and unnormalised output O~, each rescaled by
  *                        e^(m_old - m_new), one division at the end, LSE = m + ln l
@@ -296,6 +305,86 @@ int oracle_decode_cascade(const uint16_t* q, const uint16_t* Kpre, const uint16_
                 int64_t off = (((int64_t)pg * page_size + in_page) * Hkv + kvh) * d;
                 kr[n] = Kp + off;
                 vr[n] = Vp + off;
+            }
+            if (bad) {
+#pragma omp atomic write
+                err = -2;
+                continue;
+            }
+            widen_row(q + p * d, d, dtype, qq);
+            attend_row(qq, kr, vr, n, d, dtype, scale, s, tmp, O + t * d, LSE + t, NULL);
+        }
+        free(s); free(qq); free(tmp); free(kr); free(vr);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------ paged / varlen prefill
+ * q [total_q, Hq, d]: the new queries of all requests, packed (cu_seqlens_q [B+1], rows of
+ * request r are cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1).  The pools and block_table are as in
+ * oracle_decode_paged; kv_lens[r] counts the cached tokens of request r, including its
+ * q_len new ones.  rows: flat indices (token * Hq + h) to evaluate (NULL = all
+ * total_q * Hq).  Returns 0, -1 on bad arguments, -2 if a needed table entry is outside
+ * [0, num_pages).                                                                          */
+int oracle_prefill_paged(const uint16_t* q, const uint16_t* Kp, const uint16_t* Vp,
+                         const int32_t* block_table, const int32_t* cu_seqlens_q,
+                         const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int page_size,
+                         int max_pages, int64_t num_pages, int total_q, int causal,
+                         double scale, int dtype, const int64_t* rows, int64_t n_rows,
+                         double* O, double* LSE)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || Hq % Hkv) return -1;
+    if (total_q < 0 || cu_seqlens_q[0] != 0 || cu_seqlens_q[B] > total_q) return -1;
+    int max_kv = 0;
+    for (int r = 0; r < B; ++r) {
+        if (cu_seqlens_q[r + 1] < cu_seqlens_q[r]) return -1;
+        if (kv_lens[r] < 0 || kv_lens[r] > (int64_t)max_pages * page_size) return -1;
+        if (kv_lens[r] > max_kv) max_kv = kv_lens[r];
+    }
+    const int64_t total = (int64_t)total_q * Hq;
+    if (!rows) n_rows = total;
+    const int group = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        int cap = max_kv > 0 ? max_kv : 1;
+        double* s = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* qq = (double*)malloc(sizeof(double) * (size_t)d);
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+        const uint16_t** kr = (const uint16_t**)malloc(sizeof(void*) * (size_t)cap);
+        const uint16_t** vr = (const uint16_t**)malloc(sizeof(void*) * (size_t)cap);
+        const int ok = s && qq && tmp && kr && vr;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n_rows; ++t) {
+            int64_t p = rows ? rows[t] : t;
+            int tok = (int)(p / Hq), h = (int)(p % Hq);
+            int r = -1;
+            if (ok && p >= 0 && p < total)
+                for (int k = 0; k < B; ++k)
+                    if (cu_seqlens_q[k] <= tok && tok < cu_seqlens_q[k + 1]) { r = k; break; }
+            if (r < 0) {     /* a padding row past the last request, or a bad index */
+#pragma omp atomic write
+                err = -1;
+                continue;
+            }
+            int kvh = h / group;
+            int q_len = cu_seqlens_q[r + 1] - cu_seqlens_q[r];
+            int i = tok - cu_seqlens_q[r];
+            int kv_len = kv_lens[r];
+            /* keys visible to new query i: positions 0 .. kv_len - q_len + i (causal) */
+            int n = kv_len;
+            if (causal) {
+                int last = kv_len - q_len + i;
+                n = last + 1 < 0 ? 0 : (last + 1 < kv_len ? last + 1 : kv_len);
+            }
+            int bad = 0;
+            for (int key = 0; key < n; ++key) {
+                int32_t pg = block_table[(int64_t)r * max_pages + key / page_size];
+                int in_page = key % page_size;
+                if (pg < 0 || pg >= num_pages) { bad = 1; break; }
+                int64_t off = (((int64_t)pg * page_size + in_page) * Hkv + kvh) * d;
+                kr[key] = Kp + off;
+                vr[key] = Vp + off;
             }
             if (bad) {
 #pragma omp atomic write

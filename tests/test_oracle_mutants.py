@@ -34,6 +34,10 @@ MUTANTS = {
     "cascade_drops_prefix": ("for (int tok = 0; tok < prefix_len; ++tok, ++n) {",
                              "for (int tok = 0; tok < 0; ++tok, ++n) {"),
     "cascade_own_tokens_wrong_slot": ("int in_page = tok % page_size;", "int in_page = (tok + 3) % page_size;"),
+    "paged_prefill_top_left_mask": ("int last = kv_len - q_len + i;", "int last = i;"),
+    "paged_prefill_row_not_rebased": ("int i = tok - cu_seqlens_q[r];", "int i = tok;"),
+    "paged_prefill_wrong_kv_slot": ("int in_page = key % page_size;",
+                                    "int in_page = (key + 1) % page_size;"),
 }
 
 PINS = [
@@ -51,6 +55,7 @@ PINS = [
     pins.test_bsr_example_paged_equals_contiguous_exactly,
     pins.test_decode_matches_torch_sdpa_and_is_page_order_free,
     pins.test_cascade_matches_torch_sdpa_over_prefix_then_own_tokens,
+    lambda: pins.test_paged_prefill_matches_torch_sdpa_bottom_right(True),
 ]
 
 

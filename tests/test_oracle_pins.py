@@ -20,7 +20,7 @@ import torch.nn.functional as F
 
 import oracle
 from attn_inputs import (BF16, FP16, bits_to_f64, decode_case, f32_to_bf16_bits, normal_bits,
-                         permute_pages, prefill_case)
+                         paged_prefill_case, permute_pages, prefill_case)
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -419,3 +419,115 @@ def test_cascade_equals_merge_of_prefix_and_own_states():
             Om, Lm = oracle.merge(np.stack([Opre[r, h], Oown[r, h]]), np.array([Lpre[r, h], Lown[r, h]]))
             np.testing.assert_allclose(O[r, h], Om, rtol=1e-12, atol=1e-13)
             np.testing.assert_allclose(L[r, h], Lm, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- paged / varlen prefill
+# [LLM Internals 10.3.8, variable-length batching; 10.3.7 block table; CS349D Lecture 4
+# section 5.1, incremental prefill] new queries packed end to end by cu_seqlens_q, each
+# request's cache holding its history followed by its new tokens.
+
+def _gather_request(case, r):
+    """Request r's cached K/V as contiguous fp64 [Hkv, kv_len, d] (by plain indexing)."""
+    n = int(case.kv_lens[r])
+    toks = np.arange(n)
+    pages = case.block_table[r, toks // case.page_size]
+    k = bits_to_f64(case.k_pages[pages, toks % case.page_size], case.dtype).transpose(1, 0, 2)
+    v = bits_to_f64(case.v_pages[pages, toks % case.page_size], case.dtype).transpose(1, 0, 2)
+    return k, v
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_paged_prefill_matches_torch_sdpa_bottom_right(causal):
+    # requests: a chunk after history, a whole prompt (q_len = kv_len), a decode step
+    # (q_len = 1), an empty chunk, a chunk crossing page boundaries
+    case = paged_prefill_case(8, 2, 16, [5, 19, 1, 0, 33], [40, 19, 23, 7, 50], dtype=BF16,
+                              causal=causal, seeds=(81, 82, 83))
+    O, L = oracle.prefill_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                case.cu_seqlens_q, case.kv_lens, causal, case.scale, BF16)
+    for r in range(case.B):
+        ql, kl = int(case.q_lens[r]), int(case.kv_lens[r])
+        if ql == 0:
+            continue
+        k, v = _gather_request(case, r)
+        rows = slice(case.cu_seqlens_q[r], case.cu_seqlens_q[r + 1])
+        qv = bits_to_f64(case.q[rows], BF16).transpose(1, 0, 2)[None]      # [1, Hq, ql, d]
+        # torch's own mask: query i sees key j iff j <= kl - ql + i (bottom-right)
+        mask = None
+        if causal:
+            mask = torch.from_numpy(np.arange(kl)[None, :] <= (kl - ql + np.arange(ql))[:, None])
+        o = F.scaled_dot_product_attention(torch.from_numpy(qv), torch.from_numpy(k[None]),
+                                           torch.from_numpy(v[None]), attn_mask=mask,
+                                           scale=case.scale, enable_gqa=True)
+        np.testing.assert_allclose(O[rows], o.numpy()[0].transpose(1, 0, 2), rtol=1e-12,
+                                   atol=1e-12)
+        s = case.scale * np.einsum("hid,hnd->hin", qv[0], np.repeat(k, 4, axis=0))
+        if causal:
+            s = np.where(mask.numpy()[None], s, -np.inf)
+        np.testing.assert_allclose(L[rows], sps.logsumexp(s, axis=-1).T, rtol=1e-12, atol=1e-12)
+
+
+def test_paged_prefill_packing_example_and_isolation():
+    # lengths 3, 5, 2 pack as [0, 3, 8, 10] [LLM Internals 10.3.8]; changing one request's
+    # cache leaves the others' outputs bitwise unchanged (the sequences do not see each other)
+    case = paged_prefill_case(4, 4, 8, [3, 5, 2], [3, 21, 9], dtype=FP16, seeds=(84, 85, 86))
+    assert case.cu_seqlens_q.tolist() == [0, 3, 8, 10]
+    O, L = oracle.prefill_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                case.cu_seqlens_q, case.kv_lens, True, case.scale, FP16)
+    kp = case.k_pages.copy()
+    vp = case.v_pages.copy()
+    own = case.block_table[1, :2]
+    kp[own] = normal_bits(kp[own].shape, 87, FP16)
+    vp[own] = normal_bits(vp[own].shape, 88, FP16)
+    O2, L2 = oracle.prefill_paged(case.q, kp, vp, case.block_table, case.cu_seqlens_q,
+                                  case.kv_lens, True, case.scale, FP16)
+    for rows in (slice(0, 3), slice(8, 10)):
+        assert np.array_equal(O[rows], O2[rows]) and np.array_equal(L[rows], L2[rows])
+    assert not np.array_equal(O[3:8], O2[3:8])
+
+
+def test_paged_prefill_zero_queries_count_visible_keys():
+    # q = 0: every score is 0, so LSE = ln(number of visible keys) = ln(kv - q_len + i + 1)
+    case = paged_prefill_case(4, 2, 8, [7, 1, 16], [7, 30, 40], seeds=(89, 90, 91))
+    q0 = np.zeros_like(case.q)
+    _, L = oracle.prefill_paged(q0, case.k_pages, case.v_pages, case.block_table,
+                                case.cu_seqlens_q, case.kv_lens, True, case.scale, BF16)
+    for r in range(case.B):
+        ql, kl = int(case.q_lens[r]), int(case.kv_lens[r])
+        for i in range(ql):
+            row = case.cu_seqlens_q[r] + i
+            assert np.all(np.round(np.exp(L[row])) == kl - ql + i + 1)
+
+
+def test_paged_prefill_of_a_whole_prompt_is_causal_attention():
+    # q_len = kv_len: the chunk is the whole prompt, i.e. ordinary causal prefill
+    N = 45
+    case = paged_prefill_case(6, 3, 16, [N], [N], dtype=BF16, seeds=(92, 93, 94))
+    O, L = oracle.prefill_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                case.cu_seqlens_q, case.kv_lens, True, case.scale, BF16)
+    k, v = _gather_request(case, 0)
+    q = case.q.transpose(1, 0, 2)[None]
+    toks = np.arange(N)
+    pages = case.block_table[0, toks // 16]
+    kb = case.k_pages[pages, toks % 16].transpose(1, 0, 2)[None]
+    vb = case.v_pages[pages, toks % 16].transpose(1, 0, 2)[None]
+    Od, Ld = oracle.attention(q, kb, vb, True, case.scale, BF16)
+    np.testing.assert_allclose(O, Od[0].transpose(1, 0, 2), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(L, Ld[0].T, rtol=1e-13, atol=1e-13)
+
+
+def test_paged_prefill_rejects_padding_rows_and_handles_short_caches():
+    # rows past the last request are not anyone's query
+    case = paged_prefill_case(2, 1, 8, [2, 3], [4, 3], pad_q=2, seeds=(95, 96, 97))
+    with pytest.raises(ValueError):
+        oracle.prefill_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                             case.cu_seqlens_q, case.kv_lens, True, case.scale, BF16)
+    O, L = oracle.prefill_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                case.cu_seqlens_q, case.kv_lens, True, case.scale, BF16,
+                                rows=np.arange(5 * 2))
+    assert np.all(np.isfinite(L))
+    # a cache shorter than the chunk: the first new queries see no key (O = 0, LSE = -inf)
+    case = paged_prefill_case(2, 1, 8, [4], [2], seeds=(98, 99, 100))
+    O, L = oracle.prefill_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                case.cu_seqlens_q, case.kv_lens, True, case.scale, BF16)
+    assert np.all(L[:2] == -np.inf) and np.all(O[:2] == 0.0)
+    assert np.all(np.isfinite(L[2:]))
