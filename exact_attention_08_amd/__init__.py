@@ -61,6 +61,9 @@ _lib.attn_decode_cascade.argtypes = [_P, _P, _P, _i, _P, _P, _P, _P, _P, _P, _i,
 _lib.attn_decode_cascade.restype = _i
 _lib.attn_decode_cascade_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.attn_decode_cascade_workspace_bytes.restype = _sz
+_lib.attn_prefill_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i,
+                                    _i, _f, _i, _P]
+_lib.attn_prefill_paged.restype = _i
 
 ATTN_OK = 0
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
@@ -68,7 +71,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -7: "ATTN_ERR_HIP"}
 ATTN_BF16, ATTN_FP16 = 0, 1
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
-           "attn_decode_cascade", "attn_decode_cascade_workspace_bytes")
+           "attn_decode_cascade", "attn_decode_cascade_workspace_bytes", "attn_prefill_paged")
 
 
 class AttnError(RuntimeError):
@@ -213,3 +216,41 @@ def attn_decode_cascade(q, k_prefix, v_prefix, k_pages, v_pages, block_table, ct
                                     workspace.data_ptr(), ws_bytes, _stream_ptr(q, stream))
     _check("attn_decode_cascade", code)
 
+
+
+def attn_prefill_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens, O, LSE,
+                       max_q_len: int, causal: bool = True, scale: float | None = None,
+                       stream=None) -> None:
+    """O (and LSE unless None) <- prefill of each request's new tokens (rows
+    cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 of q [total_q, Hq, d]) over its paged cache of
+    kv_lens[r] tokens, the new ones last.  max_q_len bounds every request's q_len."""
+    import torch
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q),
+                    ("kv_lens", kv_lens), ("O", O)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(q.dim() == 3 and O.shape == q.shape, "q,O must be [total_q,Hq,d]")
+    total_q, Hq, d = q.shape
+    _need(k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "pages must be [P,page,Hkv,d]")
+    _, page, Hkv, d2 = k_pages.shape
+    _need(d2 == d, "page head dim must match q")
+    _need(kv_lens.dtype == torch.int32 and kv_lens.dim() == 1, "kv_lens must be int32 [B]")
+    B = kv_lens.shape[0]
+    _need(cu_seqlens_q.dtype == torch.int32 and tuple(cu_seqlens_q.shape) == (B + 1,),
+          "cu_seqlens_q must be int32 [B+1]")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+          "block_table must be int32 [B,max_pages]")
+    if LSE is not None:
+        _need(LSE.is_cuda and LSE.is_contiguous() and LSE.dtype == torch.float32 and
+              tuple(LSE.shape) == (total_q, Hq), "LSE must be fp32 [total_q,Hq]")
+    dt = _dtype_code(q)
+    _need(all(t.dtype == q.dtype for t in (k_pages, v_pages, O)), "dtypes must match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _lib.attn_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                   block_table.data_ptr(), cu_seqlens_q.data_ptr(),
+                                   kv_lens.data_ptr(), O.data_ptr(),
+                                   None if LSE is None else LSE.data_ptr(), B, Hq, Hkv, d, page,
+                                   block_table.shape[1], int(max_q_len), int(bool(causal)),
+                                   float(scale), dt, _stream_ptr(q, stream))
+    _check("attn_prefill_paged", code)

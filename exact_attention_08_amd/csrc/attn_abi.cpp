@@ -147,3 +147,37 @@ extern "C" int attn_decode_cascade(const void* q, const void* Kprefix, const voi
                        workspace, stream, Kprefix, Vprefix, prefix_len};
     return attn::launch_decode(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
+
+extern "C" int attn_prefill_paged(const void* q, const void* Kpages, const void* Vpages,
+                                  const int* block_table, const int* cu_seqlens_q,
+                                  const int* kv_lens, void* O, float* LSE, int B, int Hq,
+                                  int Hkv, int d, int page_size, int max_pages_per_seq,
+                                  int max_q_len, int causal, float scale, int dtype,
+                                  void* stream) {
+    if (!q || !Kpages || !Vpages || !block_table || !cu_seqlens_q || !kv_lens || !O)
+        return ATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
+        max_q_len < 0 || Hq % Hkv != 0)
+        return ATTN_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+    // one request's query rows are addressed with 32-bit byte offsets; the grid, the page
+    // offsets within a request and the packed row indices stay in 32 bits
+    if ((long long)max_q_len * Hq * d * 2 > (1LL << 30) ||
+        (long long)max_pages_per_seq * page_size > 0x7fffffffLL ||
+        (long long)B * Hkv > 0x7fffffffLL || (long long)Hkv * d * 2 * 16 > 0x7fffffffLL)
+        return ATTN_ERR_SHAPE;
+    const long long n_qtiles = ((long long)max_q_len * (Hq / Hkv) + 127) / 128;
+    if (n_qtiles * B * Hkv > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(Kpages, 16) || !aligned(Vpages, 16) || !aligned(O, 16) ||
+        !aligned(block_table, 4) || !aligned(cu_seqlens_q, 4) || !aligned(kv_lens, 4) ||
+        (LSE && !aligned(LSE, 4)))
+        return ATTN_ERR_ALIGN;
+    if (max_q_len == 0) return ATTN_OK;   // no request has a new token: nothing to compute
+    attn::PagedPrefillArgs a{q, Kpages, Vpages, block_table, cu_seqlens_q, kv_lens, O, LSE, B,
+                             Hq, Hkv, d, max_pages_per_seq, max_q_len, causal != 0,
+                             dtype == ATTN_BF16, scale, stream};
+    return attn::launch_prefill_paged(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}

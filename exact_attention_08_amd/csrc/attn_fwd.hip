@@ -121,23 +121,40 @@ template <int D> __device__ __forceinline__ int v_swz(int r) {
 // r * G + g), so the prefix keys are read once for all of them; an item sweeps one chunk of
 // the prefix (non-causal) and writes its partial state -- O normalised, in fp32, and LSE --
 // among the split partials that the decode merge combines.
-struct CascadeGeo {
-    int n_rows;     // query rows per kv head (requests x G)
+struct ModeGeo {
+    int n_rows;     // prefix mode: query rows per kv head (requests x G); paged: max q_len
     int chunk;      // prefix keys per item
     int n_chunks;
     int s_stride;   // partial states per (request, query head)
     int s_base;     // index of the first prefix chunk among them
 };
 
-// CASC selects the shared-prefix mode: Q is the decode query q [B, Hq, d], K/V the prefix
-// [Hkv, N, d], O (as fp32) and LSE the partial-state buffers.
-template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST, bool CASC>
+// Paged / varlen prefill [LLM Internals 10.3.8, variable-length batching; 10.3.7, block
+// table; CS349D Lecture 4 section 5.1, incremental prefill].  Request r's new queries are
+// rows cu_q[r] .. cu_q[r+1]-1 of q [total_q, Hq, d]; its cache holds kv_lens[r] tokens in
+// 16-token pages, the new ones last, so new query i sits at position kv_len - q_len + i and
+// (causal) sees the keys up to it.  An item is (request, kv head, tile of 128 rows); as in
+// the prefix mode the G query heads share the tile (row t = query t / G, head t % G), so
+// each K/V byte is read once per tile, and wave w streams page w of each 64-key tile with a
+// descriptor that ends at the page's last valid slot: slots past the cache read as zero.
+
+enum { kModeDense = 0, kModePrefix = 1, kModePaged = 2 };
+
+// MODE kModePrefix is the shared-prefix mode: Q is the decode query q [B, Hq, d], K/V the
+// prefix [Hkv, N, d], O (as fp32) and LSE the partial-state buffers.  kModePaged: Q is q
+// [total_q, Hq, d], K/V the page pools [pages, 16, Hkv, d], O [total_q, Hq, d], LSE
+// [total_q, Hq] or null.
+template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST, int MODE>
 __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int B, int Hq, int Hkv, int N, float scale_log2, int n_qtiles, int n_items, int xcd_major,
-    CascadeGeo cg) {
+    ModeGeo cg, const int* __restrict__ pg_table, const int* __restrict__ pg_cu_q,
+    const int* __restrict__ pg_kv_lens, int pg_max_pages) {
+    constexpr bool CASC = MODE == kModePrefix;
+    constexpr bool PAGED = MODE == kModePaged;
     static_assert(!CASC || (!CAUSAL && !PERSIST), "the prefix mode is non-causal, one item per workgroup");
+    static_assert(!PAGED || !PERSIST, "the paged mode runs one item per workgroup");
     using E = Elem<IS_BF16>;
     constexpr int BC = PrefillTile<D>::BC;
     constexpr int kQB = PrefillTile<D>::QB;
@@ -151,6 +168,8 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     constexpr int STAGE_B = 2 * TILE_B;  // one LDS stage: the K tile, then the V tile
     constexpr int NDMA = TILE_B / 1024 / kWaves;   // 1 KiB wave loads per tile and wave
     static_assert(NDMA * 1024 * kWaves == TILE_B, "K/V tile must split into 1 KiB wave loads");
+    static_assert(!PAGED || (BC == 16 * kWaves && NDMA * 1024 == 16 * RB),
+                  "paged mode: each wave loads one 16-token page of a tile");
 
     __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGE_B];   // two stages of STAGE_B bytes
 
@@ -203,35 +222,57 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 c.b = 0;
                 c.h = 0;
                 return c;
+            } else if constexpr (PAGED) {
+                return prefill_work_item((int)blockIdx.x, n_qtiles, Hkv, 1, xcd_major);
             } else {
                 return prefill_work_item(slot * P + x, n_qtiles, Hkv, G, xcd_major);
             }
         }();
+        // paged mode: the request's packed query rows and cache length (clamped to what the
+        // launch and the block table cover)
+        int pq0 = 0, pq_len = 0, pkv_len = 0;
+        if constexpr (PAGED) {
+            pq0 = __builtin_amdgcn_readfirstlane(pg_cu_q[wi.b]);
+            pq_len = min(max(__builtin_amdgcn_readfirstlane(pg_cu_q[wi.b + 1]) - pq0, 0), cg.n_rows);
+            pkv_len = min(max(__builtin_amdgcn_readfirstlane(pg_kv_lens[wi.b]), 0), pg_max_pages * 16);
+        }
         const int64_t qh_off = ((int64_t)wi.b * Hq + wi.h) * (int64_t)N;      // row offset of (b,h)
         const int64_t kh_off = ((int64_t)wi.b * Hkv + wi.kvh) * (int64_t)N;   // row offset of (b,kvh)
         const int head_bytes = N * D * 2;
-        const int q_bytes = CASC ? B * Hq * D * 2 : head_bytes;
-        const __amdgpu_buffer_rsrc_t rq = head_rsrc(CASC ? Q : Q + qh_off * D, q_bytes);
+        const int q_bytes = CASC ? B * Hq * D * 2 : PAGED ? pq_len * Hq * D * 2 : head_bytes;
+        const __amdgpu_buffer_rsrc_t rq = head_rsrc(
+            CASC ? Q : PAGED ? Q + (int64_t)pq0 * Hq * D : Q + qh_off * D, q_bytes);
 
         const int q_tile0 = wi.qt * kBR;
         const int q0w = q_tile0 + wave * (32 * kQB);   // first query row of this wave
-        const int n_qrows = CASC ? cg.n_rows : N;
+        const int n_qrows = CASC ? cg.n_rows : PAGED ? pq_len * G : N;
         const bool wave_live = q0w < n_qrows;
+        if (PAGED && q_tile0 >= n_qrows) break;        // a tile past this request's rows
 
-        // Keys of the item: [kbase, kend) (a prefix chunk, or the whole sequence).  KV tiles
-        // this workgroup visits: causal stops after the block holding its last row.
+        // Keys of the item: [kbase, kend) (a prefix chunk, the request's cache, or the whole
+        // sequence).  KV tiles this workgroup visits: causal stops after the block holding
+        // its last row.
         const int kbase = CASC ? chunk_id * cg.chunk : 0;
-        const int kend = CASC ? min(N, kbase + cg.chunk) : N;
-        const int kv_last = CAUSAL ? min(N, q_tile0 + kBR) - 1 : kend - 1;
-        const int n_kv = (kv_last - kbase) / BC + 1;
+        const int kend = CASC ? min(N, kbase + cg.chunk) : PAGED ? pkv_len : N;
+        // paged: row t is query t / G at position pq_pos0 + t / G
+        const int pq_pos0 = pkv_len - pq_len;
+        int kv_last, n_kv;
+        if constexpr (PAGED) {
+            const int t_last = min(q_tile0 + kBR, n_qrows) - 1;
+            kv_last = CAUSAL ? min(kend, pq_pos0 + t_last / G + 1) - 1 : kend - 1;
+            n_kv = kv_last < 0 ? 1 : kv_last / BC + 1;
+        } else {
+            kv_last = CAUSAL ? min(N, q_tile0 + kBR) - 1 : kend - 1;
+            n_kv = (kv_last - kbase) / BC + 1;
+        }
         const int wave_last_q = min(q0w + 32 * kQB - 1, n_qrows - 1);
 
         // a2: this lane's Q rows (one per column block) as the B operand of S^T = K Q^T
         // (k-values d = 16ks + 8g..+7); rows past the last query read as zero (offset past
         // the buffer range)
         auto q_offset = [&](int t, int ks) {
-            if constexpr (CASC) {
-                if (t >= cg.n_rows) return q_bytes;
+            if constexpr (CASC || PAGED) {
+                if (t >= n_qrows) return q_bytes;
                 const int rr = t / G;
                 return ((rr * Hq + wi.kvh * G + (t - rr * G)) * D + ks * 16 + g * 8) * 2;
             } else {
@@ -255,6 +296,31 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)lds);
         auto dma_tile = [&](int j, int st) {
             const int key0 = kbase + j * BC;
+            if constexpr (PAGED) {
+                // this wave's page: tile rows 16 wave .. 16 wave + 15, LDS blocks
+                // wave * NDMA + i; the descriptor ends at the page's last valid slot
+                const int pkey = key0 + 16 * wave;
+                const int valid = min(max(kend - pkey, 0), 16);
+                const int phys = __builtin_amdgcn_readfirstlane(
+                    valid > 0 ? pg_table[(int64_t)wi.b * pg_max_pages + pkey / 16] : 0);
+                const int64_t pbase = ((int64_t)phys * 16 * Hkv + wi.kvh) * D;
+                const int pbytes = valid > 0 ? ((valid - 1) * Hkv * D + D) * 2 : 0;
+                const i32x4 rpk = head_rsrc4(K + pbase, pbytes);
+                const i32x4 rpv = head_rsrc4(V + pbase, pbytes);
+    #pragma unroll
+                for (int i = 0; i < NDMA; ++i) {
+                    const int blk = wave * NDMA + i;
+                    const int p = blk * 64 + lane;
+                    const int r = p / NSLOT, sl = p % NSLOT;
+                    const int slot_ofs = (r - 16 * wave) * Hkv * D;
+                    const int kofs = (slot_ofs + 8 * (sl ^ k_swz<D>(r))) * 2;
+                    const int vofs = (slot_ofs + 8 * (sl ^ v_swz<D>(r))) * 2;
+                    const uint32_t kdst = __builtin_amdgcn_readfirstlane(lds_base + st * STAGE_B + blk * 1024);
+                    dma_b128(rpk, kdst, kofs);
+                    dma_b128(rpv, kdst + TILE_B, vofs);
+                }
+                return;
+            }
     #pragma unroll
             for (int i = 0; i < NDMA; ++i) {
                 const int blk = i * kWaves + wave;
@@ -295,7 +361,18 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         // wave; it still takes part in the tile loads and barriers.  Near the end the "next"
         // S^T is computed on the current block and discarded, keeping step 4 branch free.
         const int nb = n_kv * NKB;
-        const int nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, wave_last_q / 32 + 1) : nb);
+        int nb_live;
+        // paged: positions of the wave's first row and of each of this lane's rows
+        int pos_first = 0, qpos[kQB];
+        if constexpr (PAGED) {
+            const int pos_last = pq_pos0 + wave_last_q / G;
+            nb_live = !wave_live ? 0 : !CAUSAL ? nb : pos_last < 0 ? 0 : min(nb, pos_last / 32 + 1);
+            pos_first = pq_pos0 + q0w / G;
+    #pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) qpos[qb] = pq_pos0 + (q0w + 32 * qb + l32) / G;
+        } else {
+            nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, wave_last_q / 32 + 1) : nb);
+        }
 
         // V^T operand of the second product from V (rows in key order) with the transposing LDS read
         // (ds_read_b64_tr_b16): within each 16-lane group G, destination lane i receives, as
@@ -366,12 +443,13 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                     }
                 if (kb + 1 < NKB) read_k(ka, ST, kb + 1);
                 // 2. statistics
-                const bool mask_blk = (CAUSAL && kfirst + 31 > q0w) || kfirst + 32 > kend;
+                const bool mask_blk = (CAUSAL && kfirst + 31 > (PAGED ? pos_first : q0w)) ||
+                                      kfirst + 32 > kend;
     #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
                     // a5: elementwise mask (select, never multiply)
                     if (mask_blk) {
-                        const int q = q0w + 32 * qb + l32;
+                        const int q = PAGED ? qpos[qb] : q0w + 32 * qb + l32;
     #pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const int key = kfirst + 8 * (v >> 2) + 4 * g + (v & 3);
@@ -390,7 +468,10 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                         const float m_blk = fmaxf(mloc, xor_lanes(mloc, 32)) * scale_log2;
                         const bool move = m_blk > m_ref[qb] + kRescaleSlack;
                         const float m_new = move ? m_blk : m_ref[qb];
-                        const float alpha = fast_exp2(m_ref[qb] - m_new);   // 0 on the first block
+                        // 0 on the first block; a paged row that has seen no key yet
+                        // (reference still -inf) keeps alpha = 1
+                        const float alpha = (PAGED && m_new == -INFINITY)
+                                                ? 1.f : fast_exp2(m_ref[qb] - m_new);
                         l_run[qb] *= alpha;
     #pragma unroll
                         for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
@@ -485,6 +566,25 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 if (g == 0) LSE[pidx] = (m_ref[qb] + fast_log2(l_tot)) * kLn2;
                 continue;
             }
+            if constexpr (PAGED) {
+                // query q / G of the request, head kvh * G + q % G; a row that sees no key
+                // (a cache shorter than its chunk) gets O = 0 and LSE = -inf
+                const int qi = q / G;
+                const int64_t row = (int64_t)(pq0 + qi) * Hq + wi.kvh * G + (q - qi * G);
+                const float inv_p = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                uint16_t* prow = O + row * D;
+    #pragma unroll
+                for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const f32x16& o = oacc[qb][db];
+                        const u32x2 w = {E::pack2(o[4 * a + 0] * inv_p, o[4 * a + 1] * inv_p),
+                                         E::pack2(o[4 * a + 2] * inv_p, o[4 * a + 3] * inv_p)};
+                        *reinterpret_cast<u32x2*>(prow + db * 32 + 8 * a + 4 * g) = w;
+                    }
+                if (g == 0 && LSE) LSE[row] = (m_ref[qb] + fast_log2(l_tot)) * kLn2;
+                continue;
+            }
             uint16_t* orow = O + (qh_off + q) * D;
     #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -520,14 +620,16 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     const long long grid = persistent && n_items > slots ? slots : n_items;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     if (grid < n_items)
-        return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, true, false>,
+        return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, true, kModeDense>,
                              dim3((unsigned)grid), dim3(kThreads), (hipStream_t)a.stream,
                              "prefill_fwd_kernel", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv,
-                             a.N, scale_log2, n_qtiles, (int)n_items, xcd_major, CascadeGeo{});
-    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, false>,
+                             a.N, scale_log2, n_qtiles, (int)n_items, xcd_major, ModeGeo{},
+                             nullptr, nullptr, nullptr, 0);
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, kModeDense>,
                          dim3((unsigned)grid), dim3(kThreads), (hipStream_t)a.stream,
                          "prefill_fwd_kernel", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N,
-                         scale_log2, n_qtiles, (int)n_items, xcd_major, CascadeGeo{});
+                         scale_log2, n_qtiles, (int)n_items, xcd_major, ModeGeo{}, nullptr,
+                         nullptr, nullptr, 0);
 }
 
 template <int D, bool IS_BF16>
@@ -537,12 +639,31 @@ hipError_t launch_cascade_prefix_t(const CascadePrefixArgs& a) {
     const int n_qtiles = (n_rows + kBR - 1) / kBR;
     const long long n_items = (long long)n_qtiles * a.Hkv * a.n_chunks;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const CascadeGeo cg{n_rows, a.chunk, a.n_chunks, a.s_stride, a.s_base};
-    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, false, false, true>,
+    const ModeGeo cg{n_rows, a.chunk, a.n_chunks, a.s_stride, a.s_base};
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, false, false, kModePrefix>,
                          dim3((unsigned)n_items), dim3(kThreads), (hipStream_t)a.stream,
                          "prefill_fwd_kernel(prefix)", a.q, a.Kprefix, a.Vprefix,
                          reinterpret_cast<uint16_t*>(a.ws_o), a.ws_lse, a.B, a.Hq, a.Hkv,
-                         a.prefix_len, scale_log2, n_qtiles, (int)n_items, 0, cg);
+                         a.prefix_len, scale_log2, n_qtiles, (int)n_items, 0, cg, nullptr,
+                         nullptr, nullptr, 0);
+}
+
+template <int D, bool IS_BF16, bool CAUSAL>
+hipError_t launch_prefill_paged_t(const PagedPrefillArgs& a) {
+    constexpr int kBR = 32 * PrefillTile<D>::QB * kWaves;
+    const int G = a.Hq / a.Hkv;
+    const long long n_qtiles = ((long long)a.max_q_len * G + kBR - 1) / kBR;
+    const int n_hg = a.B * a.Hkv;
+    const long long n_items = n_qtiles * n_hg;
+    const int xcd_major = (n_hg % 8 == 0) ? 1 : 0;
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    ModeGeo cg{};
+    cg.n_rows = a.max_q_len;
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, kModePaged>,
+                         dim3((unsigned)n_items), dim3(kThreads), (hipStream_t)a.stream,
+                         "prefill_fwd_kernel(paged)", a.q, a.Kpages, a.Vpages, a.O, a.LSE, a.B,
+                         a.Hq, a.Hkv, 0, scale_log2, (int)n_qtiles, (int)n_items, xcd_major, cg,
+                         a.block_table, a.cu_seqlens_q, a.kv_lens, a.max_pages);
 }
 
 }  // namespace
@@ -557,6 +678,19 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.is_bf16) return a.causal ? launch_prefill_t<64, true, true>(a)
                                    : launch_prefill_t<64, true, false>(a);
     return a.causal ? launch_prefill_t<64, false, true>(a) : launch_prefill_t<64, false, false>(a);
+}
+
+hipError_t launch_prefill_paged(const PagedPrefillArgs& a) {
+    if (a.d == 128) {
+        if (a.is_bf16) return a.causal ? launch_prefill_paged_t<128, true, true>(a)
+                                       : launch_prefill_paged_t<128, true, false>(a);
+        return a.causal ? launch_prefill_paged_t<128, false, true>(a)
+                        : launch_prefill_paged_t<128, false, false>(a);
+    }
+    if (a.is_bf16) return a.causal ? launch_prefill_paged_t<64, true, true>(a)
+                                   : launch_prefill_paged_t<64, true, false>(a);
+    return a.causal ? launch_prefill_paged_t<64, false, true>(a)
+                    : launch_prefill_paged_t<64, false, false>(a);
 }
 
 hipError_t launch_cascade_prefix(const CascadePrefixArgs& a) {

@@ -53,6 +53,24 @@ struct CascadePrefixArgs {
     void* stream;
 };
 
+// Paged / varlen prefill: q [total_q, Hq, d] packed by cu_seqlens_q [B + 1], page pools
+// [pages, 16, Hkv, d], block_table [B, max_pages], kv_lens [B] (cached tokens, new ones
+// included), O [total_q, Hq, d], LSE [total_q, Hq] or null.
+struct PagedPrefillArgs {
+    const void* q;
+    const void* Kpages;
+    const void* Vpages;
+    const int* block_table;
+    const int* cu_seqlens_q;
+    const int* kv_lens;
+    void* O;
+    float* LSE;
+    int B, Hq, Hkv, d, max_pages, max_q_len;
+    bool causal, is_bf16;
+    float scale;
+    void* stream;
+};
+
 // Launch through hipLaunchKernel so the status reflects this launch only (a sticky error
 // left by some earlier, unrelated HIP call must not be reported as ours).  With
 // ATTN_DEBUG set in the environment a failing launch prints the runtime's message.
@@ -81,6 +99,7 @@ int device_cu_count();
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_cascade_prefix(const CascadePrefixArgs& a);
+hipError_t launch_prefill_paged(const PagedPrefillArgs& a);
 
 // Prefix keys per partial state in a cascade decode.
 constexpr int kCascadeChunk = 512;

@@ -1,8 +1,8 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
  *
- * Two compute calls follow the problem statement of the pages (a third serves requests that
- * share a prefix):
+ * Two compute calls follow the problem statement of the pages (two more serve requests that
+ * share a prefix and chunks of new tokens over a paged cache):
  *   attn_fwd           exact scaled-dot-product attention forward (prefill), computed as a
  *                      tiled, fused kernel with online softmax: Q row-blocks stay on chip
  *                      while K/V column-blocks stream past, fully masked causal blocks are
@@ -19,6 +19,10 @@
  *   attn_decode_cascade  decode for requests that share a prefix: the prefix is read once for
  *                      all of them, then merged with each request's own tokens by the LSE
  *                      rule [CS349D Lecture 4 notes 4.4, 5.3]
+ *   attn_prefill_paged  prefill of a chunk of new tokens per request over its paged KV
+ *                      cache, requests packed end to end by cumulative lengths
+ *                      [LLM Internals 10.3.8 variable-length batching, 10.3.7 block table;
+ *                      CS349D Lecture 4 notes 5.1, incremental prefill]
  *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
@@ -30,8 +34,9 @@
  *     an error, never a silent switch to slower code.
  *   - Device-resident block tables and context lengths are not read on the host and are
  *     not validated (see attn_decode_paged).
- *   - Results are bitwise deterministic for fixed inputs, shapes and split size: there are
- *     no atomics and all reductions run in a fixed order.
+ *   - Results are bitwise deterministic for fixed inputs, shapes and split size: all
+ *     reductions run in a fixed order.  (The decode's work queue takes tickets with an
+ *     atomic counter; that decides only which workgroup computes an item, not how.)
  *   - The library keeps no state between calls and may be called from several host
  *     threads on different streams.
  */
@@ -86,6 +91,44 @@ enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
              int dtype, void* stream);
+
+/*
+ * attn_prefill_paged -- prefill of new tokens over a paged KV cache (chunked prefill)
+ * [LLM Internals 10.3.8: sequences packed end to end with cumulative lengths; 10.3.7: the
+ * block table and the [blocks, page, Hkv, d] cache; CS349D Lecture 4 notes 5.1: incremental
+ * prefill, where each request brings a different number of new queries and KV length].
+ * Request r brings q_len = cu_seqlens_q[r+1] - cu_seqlens_q[r] new tokens, whose queries
+ * are rows cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 of q.  Its cache already holds kv_lens[r]
+ * tokens, the new ones last (written there before the call), so new query i sits at
+ * position kv_lens[r] - q_len + i.  With causal set it sees the keys at positions up to
+ * its own (q_len = 1 is a decode step, q_len = kv_len ordinary causal prefill); without,
+ * all kv_lens[r] keys.  A query that sees no key (kv_lens[r] < q_len) gets O = 0 and
+ * LSE = -inf.
+ *
+ *   q             [total_q, Hq, d]   dtype, packed queries                     (read)
+ *   Kpages,       [num_pages, page_size, Hkv, d]  dtype                       (read)
+ *   Vpages
+ *   block_table   [B, max_pages_per_seq] int32: physical page of each 16-token block of a
+ *                 request's cache                                              (read)
+ *   cu_seqlens_q  [B + 1] int32, cu_seqlens_q[0] = 0, non-decreasing          (read)
+ *   kv_lens       [B] int32, cached tokens per request (new ones included)     (read)
+ *   O             [total_q, Hq, d]   dtype; rows of requests are written, other rows are
+ *                 left untouched                                               (write)
+ *   LSE           [total_q, Hq] fp32, natural log, or NULL                     (write)
+ *   max_q_len     host-side bound on every request's q_len; 0 launches nothing
+ *   causal, scale, dtype, stream  as in attn_fwd
+ *
+ *   Supported: d in {64, 128}; page_size 16; max_q_len * Hq * d * 2 <= 2^30.  Device data
+ *   are not validated: the caller guarantees cu_seqlens_q[B] <= total_q, q_len <= max_q_len,
+ *   kv_lens[r] <= max_pages_per_seq * 16 and valid page indices for the pages a request's
+ *   cache uses.  (Out-of-range lengths are clamped to those bounds; entries of unused
+ *   pages, e.g. -1, are never read.)  Returns ATTN_OK or a negative attn_status.
+ */
+int attn_prefill_paged(const void* q, const void* Kpages, const void* Vpages,
+                       const int* block_table, const int* cu_seqlens_q, const int* kv_lens,
+                       void* O, float* LSE, int B, int Hq, int Hkv, int d, int page_size,
+                       int max_pages_per_seq, int max_q_len, int causal, float scale, int dtype,
+                       void* stream);
 
 /*
  * attn_decode_paged -- one query token per sequence over a paged KV cache, split-KV.

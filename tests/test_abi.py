@@ -137,3 +137,29 @@ def test_cascade_workspace_helper_adds_the_prefix_chunks():
     assert cw(64, 32, 128, 16, 2048, 1024, 4097) == o + ((l + 255) // 256) * 256
     assert cw(64, 32, 128, 16, 2048, 1024, -1) == 0
 
+
+
+def ppre(q=A, K=A, V=A, bt=A, cu=A, kvl=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, d=128, page=16,
+         max_pages=8, max_q=64, causal=1, scale=0.1, dtype=0):
+    return L.attn_prefill_paged(q, K, V, bt, cu, kvl, O, LSE, B, Hq, Hkv, d, page, max_pages,
+                                max_q, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(K=None), -1), (dict(V=None), -1), (dict(bt=None), -1),
+    (dict(cu=None), -1), (dict(kvl=None), -1), (dict(O=None), -1),
+    (dict(B=0), -2), (dict(Hq=7), -2), (dict(max_q=-1), -2), (dict(max_pages=0), -2),
+    (dict(scale=0.0), -2), (dict(scale=float("nan")), -2), (dict(max_q=(1 << 19) + 1), -2),
+    (dict(dtype=5), -3),
+    (dict(d=80), -4), (dict(page=32), -4),
+    (dict(q=MIS), -5), (dict(K=MIS), -5), (dict(V=MIS), -5), (dict(O=MIS), -5),
+    (dict(LSE=MIS + 1), -5),
+])
+def test_attn_prefill_paged_rejects_bad_arguments(kw, code):
+    assert ppre(**kw) == code
+
+
+def test_attn_prefill_paged_without_new_tokens_launches_nothing():
+    # max_q_len = 0 is valid and returns before any HIP call (this host has no GPU)
+    assert ppre(max_q=0) == 0
+    assert ppre(max_q=0, LSE=None) == 0
