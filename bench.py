@@ -14,8 +14,9 @@ Printed: one JSON line.  `value` is the prefill throughput in TFLOP/s (algorithm
 every K/V element of every context read once, plus q, O, block table and lengths).
 `roofline` covers the prefill kernel, `decode.roofline` the decode call; `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workloads.  Outside the step
-(skipped with --no-extra): the Llama-3-8B prefill shapes, and the shared-prefix decode
-(attn_decode_cascade) next to the same requests through attn_decode_paged.
+(skipped with --no-extra): the Llama-3-8B prefill shapes, the shared-prefix decode
+(attn_decode_cascade) next to the same requests through attn_decode_paged, and chunked
+prefill over a paged cache (attn_prefill_paged).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--cpu-seconds 10] [--no-extra]
 """
@@ -38,6 +39,7 @@ PREFILL = "gpt2_medium_b64_h16_n1024_d64_causal"
 DECODE = "paged_gqa_decode_b64_ctx512_32768"
 EXTRA = ["llama3_8b_prefill_n8192_causal", "llama3_8b_prefill_n32768_causal"]
 CASCADE = "cascade_gqa_decode_b64_prefix8192_own128_4096"
+PAGED_PREFILL = "chunked_prefill_b16_hist1024_16384_chunk256_2048"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -71,6 +73,52 @@ def cascade_bytes(c, prefix_len):
     K/V once, q read, O written, table entries, lengths and LSE."""
     own, _ = decode_bytes(c)
     return own + prefix_len * c.Hkv * c.d * 2 * 2
+
+
+def paged_prefill_flops(c):
+    """Algorithmic FLOPs of a paged / varlen prefill: 4 * Hq * d per visible (query, key)
+    pair; causal query i of a request sees kv_len - q_len + i + 1 keys."""
+    pairs = 0
+    for ql, kl in zip(c.q_lens.astype("int64"), c.kv_lens.astype("int64")):
+        ql, kl = int(ql), int(kl)
+        pairs += ql * kl if not c.causal else ql * (kl - ql) + ql * (ql + 1) // 2
+    return 4.0 * c.Hq * c.d * pairs
+
+
+def paged_prefill_figure(attn, torch, dev, log, reps=10):
+    """Chunked prefill over a paged cache (PAGED_PREFILL workload).  Returns a dict for the
+    JSON line."""
+    from attn_inputs import paged_prefill_workload
+    log(f"bench: extra figure {PAGED_PREFILL}")
+    c = paged_prefill_workload(PAGED_PREFILL)
+    q = to_dev(c.q, c.dtype)
+    kp, vp = to_dev(c.k_pages, c.dtype), to_dev(c.v_pages, c.dtype)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    cu = torch.from_numpy(c.cu_seqlens_q).to(dev)
+    kvl = torch.from_numpy(c.kv_lens).to(dev)
+    O = torch.empty_like(q)
+    L = torch.empty(c.total_q, c.Hq, dtype=torch.float32, device=dev)
+
+    def call():
+        attn.attn_prefill_paged(q, kp, vp, bt, cu, kvl, O, L, c.max_q_len, c.causal, c.scale)
+
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    assert torch.isfinite(L).all(), "paged prefill produced a non-finite LSE"
+    tf = paged_prefill_flops(c) / t / 1e12
+    return {"workload": PAGED_PREFILL, "avg_launch_us": round(t * 1e6, 1),
+            "algorithmic_flops_per_launch": paged_prefill_flops(c),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                         "kernel": "prefill_fwd_kernel<128,bf16,causal,paged>"},
+            "total_q": c.total_q, "total_kv": int(c.kv_lens.astype("int64").sum())}
 
 
 def cascade_figure(attn, torch, dev, log):
@@ -232,10 +280,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the Llama-3-8B prefill figures and the shared-prefix decode figure")
-    ap.add_argument("--only", choices=["prefill", "decode", "cascade"], default=None,
+                    help="skip the Llama-3-8B prefill, shared-prefix decode and paged prefill "
+                         "figures")
+    ap.add_argument("--only", choices=["prefill", "decode", "cascade", "paged_prefill"],
+                    default=None,
                     help="(profiling) run only one half of the step, or only the shared-prefix "
-                         "decode figure")
+                         "decode or the paged prefill figure")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -256,6 +306,10 @@ def main():
 
     if args.only == "cascade":
         print(json.dumps({"cascade_decode": cascade_figure(attn, torch, dev, log)}), flush=True)
+        return
+    if args.only == "paged_prefill":
+        print(json.dumps({"paged_prefill": paged_prefill_figure(attn, torch, dev, log, reps=20)}),
+              flush=True)
         return
 
     log("bench: generating inputs")
@@ -371,9 +425,10 @@ def main():
             del Qx, Kx, Vx, Ox, Lx
             torch.cuda.empty_cache()
 
-    casc = None
+    casc = ppre = None
     if not args.no_extra and args.only is None:
         casc = cascade_figure(attn, torch, dev, log)
+        ppre = paged_prefill_figure(attn, torch, dev, log)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -405,6 +460,7 @@ def main():
             "roofline": roof_dec},
         "extra_prefill": extra or None,
         "cascade_decode": casc,
+        "paged_prefill": ppre,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
