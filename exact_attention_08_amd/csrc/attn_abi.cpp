@@ -60,7 +60,7 @@ extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, fl
 extern "C" size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int page_size,
                                                     int max_pages_per_seq, int split_tokens) {
     if (B <= 0 || Hq <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
-        split_tokens <= 0)
+        split_tokens < 0)
         return 0;
     const long long S = attn::decode_max_splits(page_size, max_pages_per_seq, split_tokens);
     return attn::decode_workspace_bytes(B, Hq, d, S);
@@ -73,13 +73,13 @@ extern "C" int attn_decode_paged(const void* q, const void* Kpages, const void* 
                                  void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !Kpages || !Vpages || !block_table || !ctx_lens || !O) return ATTN_ERR_NULL;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
-        split_tokens <= 0 || Hq % Hkv != 0)
+        split_tokens < 0 || Hq % Hkv != 0)
         return ATTN_ERR_SHAPE;
     if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
-    if (split_tokens % page_size != 0) return ATTN_ERR_UNSUPPORTED;
+    if (split_tokens % page_size != 0) return ATTN_ERR_UNSUPPORTED;   // 0 = balanced
     if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
     const long long S = attn::decode_max_splits(page_size, max_pages_per_seq, split_tokens);
     if (S > 65535 || (long long)max_pages_per_seq * page_size > 0x7fffffffLL ||
@@ -101,7 +101,7 @@ extern "C" size_t attn_decode_cascade_workspace_bytes(int B, int Hq, int d, int 
                                                       int max_pages_per_seq, int split_tokens,
                                                       int prefix_len) {
     if (B <= 0 || Hq <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
-        split_tokens <= 0 || prefix_len < 0)
+        split_tokens < 0 || prefix_len < 0)
         return 0;
     const long long S = attn::decode_max_splits(page_size, max_pages_per_seq, split_tokens) +
                         attn::cascade_chunks(prefix_len);
@@ -119,13 +119,13 @@ extern "C" int attn_decode_cascade(const void* q, const void* Kprefix, const voi
     if (prefix_len < 0) return ATTN_ERR_SHAPE;
     if (prefix_len > 0 && (!Kprefix || !Vprefix)) return ATTN_ERR_NULL;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
-        split_tokens <= 0 || Hq % Hkv != 0)
+        split_tokens < 0 || Hq % Hkv != 0)
         return ATTN_ERR_SHAPE;
     if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
-    if (split_tokens % page_size != 0) return ATTN_ERR_UNSUPPORTED;
+    if (split_tokens % page_size != 0) return ATTN_ERR_UNSUPPORTED;   // 0 = balanced
     if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
     const long long S = attn::decode_max_splits(page_size, max_pages_per_seq, split_tokens) +
                         attn::cascade_chunks(prefix_len);

@@ -53,8 +53,9 @@ constexpr int kDecThreads = 64 * kDecWaves;
 // A wave's pages per item up to which the page sweep is unrolled (1024-token splits)
 constexpr int kSweepUnroll = 8;
 
-// Work queues of the split kernel: per launch slot, [0] the next ticket and [1] the number
-// of workgroups that have finished.  The last workgroup of a launch to finish puts the slot
+// Work queues of the split kernel: per launch slot, [0] the next ticket, [1] the number of
+// workgroups that have finished and [2] the split length the launch used (read by the merge
+// kernel when the length was chosen on the device).  The last workgroup of a launch to finish puts the slot
 // back to zero, so it is ready for a later launch without any host-side reset.
 constexpr int kDecSchedSlots = 64;
 // Batches up to this size keep their per-sequence split counts in LDS (built once per
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     const uint16_t* __restrict__ Vp, const int* __restrict__ block_table,
     const int* __restrict__ ctx_lens, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int B, int Hq, int Hkv, int max_pages, int split_tokens, int S_max, float scale_log2,
-    int sched_slot) {
+    int sched_slot, int n_workers) {
     using E = Elem<IS_BF16>;
     constexpr int NKS = D / 32;          // k-steps of S^T = K Q^T (32 dims each)
     constexpr int NDB = D / 16;          // 16-row d blocks of O^T
@@ -85,6 +86,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     __shared__ int s_pref[2][kSeqCache];   // inclusive prefix sums: full splits, partial splits
     __shared__ int s_ctx[kSeqCache];
     __shared__ int s_porder[64];            // batches <= 64: partial splits, largest first
+    __shared__ int s_split;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -120,6 +122,32 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     auto vr_off = [&](int db) {
         return kPage * RB + vt_row * RB + 16 * ((2 * db + (vt_a >> 1)) ^ v_swz(vt_row)) + 8 * (vt_a & 1);
     };
+
+    // Balanced split length (split_tokens == 0) [CS349D Lecture 4 notes 5.6: the chunk
+    // length follows from the batch's total work over the workers].  The total is
+    // T = Hkv * sum(ctx) (token, kv head) pairs and P = T / n_workers the share of one
+    // workgroup.  Each item also carries a fixed cost (loading q, merging the 8 waves'
+    // states, writing its partial; about 256 pairs' worth here), so the best length grows
+    // like sqrt(P) rather than P; the steps below are the measured best lengths on MI355X
+    // for P up to 128, 3072, 10240 and beyond.  Every workgroup derives the same value from
+    // the lengths on the device, so no host plan is needed and a captured graph stays valid
+    // when the lengths change.
+    if (split_tokens == 0) {
+        if (wave == 0) {
+            long long sum = 0;
+            for (int rr = lane; rr < B; rr += 64) sum += max(ctx_lens[rr], 0);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+            const long long per = sum * Hkv / n_workers;
+            const int len = per <= 128 ? 256 : per <= 3072 ? 512 : per <= 10240 ? 1024 : 2048;
+            if (lane == 0) {
+                s_split = len;
+                if (blockIdx.x == 0) g_decode_sched[sched_slot][2] = (unsigned)len;
+            }
+        }
+        __syncthreads();
+        split_tokens = __builtin_amdgcn_readfirstlane(s_split);
+    }
 
     // Work list.  The non-empty splits are numbered t = 0 .. n_full + n_part - 1: first the
     // full splits (split_tokens tokens) of sequence 0, 1, ..., then the shorter last split of
@@ -472,7 +500,7 @@ template <int D, bool IS_BF16>
 __global__ __launch_bounds__(D) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const int* __restrict__ ctx_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int Hq, int split_tokens, int S_max, int n_pre, int s_base) {
+    int Hq, int split_tokens, int S_max, int n_pre, int s_base, int sched_slot) {
     using E = Elem<IS_BF16>;
     constexpr int NW = D / 64;                 // waves per workgroup
     __shared__ float s_w[D];
@@ -481,6 +509,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
     const int r = rh / Hq;
     const int d = threadIdx.x;
     const int ctx = ctx_lens[r];
+    // a split length chosen on the device was left in the launch's queue slot
+    if (split_tokens == 0) split_tokens = (int)g_decode_sched[sched_slot][2];
     const int n_state = n_pre + (ctx + split_tokens - 1) / split_tokens;
     const float* lse_s = ws_lse + (int64_t)rh * S_max;
     const float* o_s = ws_o + (int64_t)rh * S_max * D;
@@ -532,7 +562,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
 template <int D, bool IS_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a) {
     // partial states per (sequence, head): the splits, then the prefix chunks (if any)
-    const long long S_split = decode_max_splits(a.page_size, a.max_pages, a.split_tokens);
+    const long long S_split = decode_max_splits(a.page_size, a.max_pages, a.split_tokens);   // 0: shortest balanced split
     const long long n_pre = a.prefix_len > 0 ? cascade_chunks(a.prefix_len) : 0;
     const long long S = S_split + n_pre;
     float* ws_o = (float*)a.workspace;
@@ -557,11 +587,11 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
                                  dim3(kDecThreads), st, "decode_split_kernel", a.q, a.Kpages,
                                  a.Vpages, a.block_table, a.ctx_lens, ws_o, ws_lse, a.B, a.Hq,
                                  a.Hkv, a.max_pages, a.split_tokens, (int)S, scale_log2,
-                                 sched_slot);
+                                 sched_slot, device_cu_count());
     if (e != hipSuccess) return e;
     return launch_kernel(decode_merge_kernel<D, IS_BF16>, dim3((unsigned)(a.B * a.Hq)), dim3(D),
                          st, "decode_merge_kernel", ws_o, ws_lse, a.ctx_lens, a.O, a.LSE, a.Hq,
-                         a.split_tokens, (int)S, (int)n_pre, (int)S_split);
+                         a.split_tokens, (int)S, (int)n_pre, (int)S_split, sched_slot);
 }
 
 }  // namespace

@@ -107,10 +107,14 @@ inline long long cascade_chunks(int prefix_len) {
     return ((long long)prefix_len + kCascadeChunk - 1) / kCascadeChunk;
 }
 
+// Shortest split the device-side balanced choice (split_tokens == 0) can pick.
+constexpr int kMinBalancedSplit = 256;
+
 // Number of splits per sequence the workspace is sized for.
 inline long long decode_max_splits(int page_size, int max_pages, int split_tokens) {
     const long long max_tokens = (long long)max_pages * page_size;
-    return (max_tokens + split_tokens - 1) / split_tokens;
+    const long long len = split_tokens > 0 ? split_tokens : kMinBalancedSplit;
+    return (max_tokens + len - 1) / len;
 }
 
 // Workspace layout: O partials [B][Hq][S][d] fp32, then LSE partials [B][Hq][S] fp32.

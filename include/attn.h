@@ -57,8 +57,8 @@ enum attn_status {
                                /* not a finite positive number                                */
     ATTN_ERR_DTYPE = -3,       /* dtype is neither ATTN_BF16 nor ATTN_FP16                     */
     ATTN_ERR_UNSUPPORTED = -4, /* valid attention, but not built here: d not in {64, 128},     */
-                               /* page_size != 16, split_tokens not a positive multiple of     */
-                               /* page_size                                                    */
+                               /* page_size != 16, split_tokens not 0 or a positive multiple  */
+                               /* of page_size                                                 */
     ATTN_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned                      */
     ATTN_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the helper's size             */
     ATTN_ERR_HIP = -7          /* the HIP runtime reported an error at launch                  */
@@ -150,13 +150,22 @@ int attn_prefill_paged(const void* q, const void* Kpages, const void* Vpages,
  *   ascending order: LSE = ln sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.
  *   A sequence with ctx_lens[r] == 0 gets O = 0 and LSE = -inf.
  *
+ *   split_tokens == 0 chooses the split on the device, balanced for the batch [CS349D
+ *   Lecture 4 notes 5.6: the chunk length follows from the batch's total work over the
+ *   workers]: with T = Hkv * sum(ctx_lens) and P = T / (compute units), the split is 256,
+ *   512, 1024 or 2048 tokens for P up to 128, 3072, 10240 and beyond.  The choice is made
+ *   from the device-resident lengths at run time, so a call captured in a HIP graph stays
+ *   valid (and balanced) when the lengths change between replays.  Results are bitwise
+ *   equal to a call with that split given explicitly.  The workspace helper sizes the
+ *   workspace for the shortest (256-token) split when given split_tokens == 0.
+ *
  *   Caller preconditions (device data, not checked): 0 <= ctx_lens[r] <=
  *   max_pages_per_seq * page_size, and every block_table entry a sequence uses
  *   (index < ceil(ctx/page_size)) is a valid page in [0, num_pages).  Entries past that are
  *   never read and may hold anything (e.g. -1).
  *
- *   Supported: d in {64, 128}; page_size == 16; split_tokens a positive multiple of
- *   page_size; dtype bf16 or fp16; Hq % Hkv == 0 with Hq / Hkv <= 16.  q, Kpages, Vpages,
+ *   Supported: d in {64, 128}; page_size == 16; split_tokens 0 (balanced) or a positive
+ *   multiple of page_size; dtype bf16 or fp16; Hq % Hkv == 0 with Hq / Hkv <= 16.  q, Kpages, Vpages,
  *   O and workspace must be 16-byte aligned; block_table, ctx_lens and LSE 4-byte aligned.
  *   Returns ATTN_OK or a negative attn_status.
  */

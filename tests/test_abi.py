@@ -77,7 +77,7 @@ def dec(q=A, K=A, V=A, bt=A, ctx=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, d=128, page=16
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(K=None), -1), (dict(V=None), -1), (dict(bt=None), -1),
     (dict(ctx=None), -1), (dict(O=None), -1),
-    (dict(B=0), -2), (dict(Hq=7), -2), (dict(max_pages=0), -2), (dict(split=0), -2),
+    (dict(B=0), -2), (dict(Hq=7), -2), (dict(max_pages=0), -2), (dict(split=-16), -2),
     (dict(scale=0.0), -2), (dict(page=0), -2),
     (dict(dtype=5), -3),
     (dict(d=80), -4), (dict(page=32), -4), (dict(page=8), -4), (dict(split=24), -4),
@@ -113,7 +113,7 @@ def casc(q=A, Kp=A, Vp=A, P=100, K=A, V=A, bt=A, ctx=A, O=A, LSE=A, B=2, Hq=8, H
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(K=None), -1), (dict(bt=None), -1), (dict(O=None), -1),
     (dict(Kp=None), -1), (dict(Vp=None), -1),
-    (dict(P=-1), -2), (dict(B=0), -2), (dict(Hq=7), -2), (dict(split=0), -2),
+    (dict(P=-1), -2), (dict(B=0), -2), (dict(Hq=7), -2), (dict(split=-16), -2),
     (dict(scale=0.0), -2), (dict(P=(1 << 22) + 1), -2),
     (dict(dtype=5), -3),
     (dict(d=80), -4), (dict(page=32), -4), (dict(split=24), -4), (dict(Hq=64, Hkv=2), -4),
@@ -163,3 +163,15 @@ def test_attn_prefill_paged_without_new_tokens_launches_nothing():
     # max_q_len = 0 is valid and returns before any HIP call (this host has no GPU)
     assert ppre(max_q=0) == 0
     assert ppre(max_q=0, LSE=None) == 0
+
+
+def test_balanced_split_workspace_is_sized_for_the_shortest_split():
+    ws = L.attn_decode_paged_workspace_bytes
+    assert ws(64, 32, 128, 16, 2048, 0) == ws(64, 32, 128, 16, 2048, 256)
+    assert ws(64, 32, 128, 16, 2048, -16) == 0
+    cw = L.attn_decode_cascade_workspace_bytes
+    assert cw(8, 32, 128, 16, 100, 0, 1000) == cw(8, 32, 128, 16, 100, 256, 1000)
+    # a workspace sized for 1024-token splits is too small for the balanced choice
+    small = ws(2, 8, 128, 16, 64, 1024)
+    assert small < ws(2, 8, 128, 16, 64, 0)
+    assert dec(split=0, max_pages=64, ws_bytes=small) == -6
