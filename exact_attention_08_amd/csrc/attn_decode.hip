@@ -13,9 +13,10 @@
 //     O = sum e^{LSE_s - LSE} O_s.
 //
 // MI355X mapping:
-//   * A fixed grid of one 8-wave workgroup per CU draws work items (sequence, split, kv head) from
-//     an atomic ticket counter, full splits first and the shorter last splits at the end,
-//     so faster workgroups take more items and the grid finishes together.  No workgroup is
+//   * A fixed grid of one 8-wave workgroup per CU takes work items (sequence, split, kv head):
+//     its first by its own index, the rest from an atomic ticket counter, full splits first
+//     and the shorter last splits at the end, so faster workgroups take more items and the
+//     grid finishes together.  No workgroup is
 //     launched for a split past a sequence's context.
 //   * The G query heads are the columns of v_mfma_f32_16x16x32 (G <= 16), the 16 slots of
 //     a page its rows: S^T = K Q^T runs on the matrix cores.  The exponentiated scores of a
@@ -153,8 +154,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     // full splits (split_tokens tokens) of sequence 0, 1, ..., then the shorter last split of
     // every sequence whose length is not a multiple of split_tokens, so the queue ends with
     // its lightest items.  Item f = t * Hkv + kvh.  Workgroups draw items from an atomic
-    // ticket counter (faster workgroups take more); a workgroup leaves once its ticket passes
-    // the item count, so the grid always drains.  Each wave derives the counts and an item's
+    // ticket counter after their first (faster workgroups take more); a workgroup leaves once
+    // its ticket passes the item count, so the grid always drains.  Each wave derives the counts and an item's
     // (r, split) from ctx_lens with wave-wide prefix sums over chunks of 64 sequences (all
     // results are wave-uniform).
     auto n_full_of = [&](int rr) { return rr < B ? ctx_lens[rr] / split_tokens : 0; };
@@ -320,9 +321,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
             P.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vofs_ld + i * RPI * slot_bytes, 0, kLoadNT);
     };
 
-    if (tid == 0) s_ticket = (int)atomicAdd(&queue[0], 1u);
-    __syncthreads();
-    int f = s_ticket;
+    // The first item of a workgroup is its own index: the dispatcher spreads workgroups
+    // round robin over the XCDs, so when there are fewer items than workgroups the busy ones
+    // are spread evenly too (first-come tickets bunched them on a few XCDs).  Later items
+    // come from the queue, numbered after the grid.
+    int f = blockIdx.x;
     Item it = setup(f);
     Page b0, b1;
     load_q(it);
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
         // published at the cross-wave merge below.  It has no value on the other threads, so
         // nothing waits for the atomic before that point.
         int next_ticket;
-        if (tid == 0) next_ticket = (int)atomicAdd(&queue[0], 1u);
+        if (tid == 0) next_ticket = (int)(gridDim.x + atomicAdd(&queue[0], 1u));
 
         float m_run = -INFINITY, l_run = 0.f;
         f32x4 oacc[NDB];
