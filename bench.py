@@ -16,7 +16,8 @@ every K/V element of every context read once, plus q, O, block table and lengths
 times the fp64 CPU oracle on a bounded sample of the same workloads.  Outside the step
 (skipped with --no-extra): the Llama-3-8B prefill shapes, the shared-prefix decode
 (attn_decode_cascade) next to the same requests through attn_decode_paged, and chunked
-prefill over a paged cache (attn_prefill_paged).
+prefill over a paged cache (attn_prefill_paged), and the read bandwidth a plain streaming
+kernel reaches (the practical HBM ceiling).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--cpu-seconds 10] [--no-extra]
 """
@@ -119,6 +120,38 @@ def paged_prefill_figure(attn, torch, dev, log, reps=10):
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
                          "kernel": "prefill_fwd_kernel<128,bf16,causal,paged>"},
             "total_q": c.total_q, "total_kv": int(c.kv_lens.astype("int64").sum())}
+
+
+def hbm_read_ceiling(torch, dev, log, gib=2, reps=5):
+    """GB/s of a plain streaming-read kernel (libhbmprobe.so) over a 2 GiB buffer: the HBM
+    bandwidth a simple kernel reaches here, as context for the decode's fraction."""
+    import ctypes
+    path = os.path.join(ROOT, "exact_attention_08_amd", "libhbmprobe.so")
+    if not os.path.exists(path):
+        log("bench: libhbmprobe.so not built; no HBM ceiling figure")
+        return None
+    lib = ctypes.CDLL(path)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    nbytes = gib << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count * 8
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert lib.hbm_read_probe(src.data_ptr(), nbytes, out.data_ptr(), blocks, st) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, out
+    torch.cuda.empty_cache()
+    return {"gbs": round(best, 1), "frac_of_peak": round(best / HBM_PEAK_GBS, 4),
+            "kernel": "hbm_read_kernel (16-byte non-temporal loads, 8 in flight per lane)",
+            "bytes": nbytes, "note": "best of 5 reads of a 2 GiB buffer"}
 
 
 def cascade_figure(attn, torch, dev, log):
@@ -425,10 +458,11 @@ def main():
             del Qx, Kx, Vx, Ox, Lx
             torch.cuda.empty_cache()
 
-    casc = ppre = None
+    casc = ppre = ceil = None
     if not args.no_extra and args.only is None:
         casc = cascade_figure(attn, torch, dev, log)
         ppre = paged_prefill_figure(attn, torch, dev, log)
+        ceil = hbm_read_ceiling(torch, dev, log)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -460,6 +494,7 @@ def main():
             "roofline": roof_dec},
         "extra_prefill": extra or None,
         "cascade_decode": casc,
+        "hbm_read_ceiling": ceil,
         "paged_prefill": ppre,
         "cpu_baseline": cpu,
     }

@@ -15,6 +15,9 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
+# the benchmark's streaming-read kernel (HBM ceiling), a library of its own
+PROBE_SRC = "hbm_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -59,6 +62,14 @@ def build(verbose: bool = False) -> str:
         subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib],
                        check=True)
         os.replace(tmp_lib, LIB)
+        tmp_probe = PROBE_LIB + ".tmp"
+        p = subprocess.run([HIPCC, *COMMON_FLAGS, "-shared", "-x", "hip",
+                            os.path.join(CSRC, PROBE_SRC), "-o", tmp_probe],
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if p.returncode != 0:
+            sys.stderr.write(p.stdout)
+            raise RuntimeError(f"hipcc failed for {PROBE_SRC}")
+        os.replace(tmp_probe, PROBE_LIB)
     return LIB
 
 
