@@ -54,6 +54,9 @@ def _bind(path: str):
     lib.oracle_decode_cascade.argtypes = [P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32,
                                           i32, i64, f64, i32, P, i64, P, P]
     lib.oracle_decode_cascade.restype = i32
+    lib.oracle_attention_variant.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, f64,
+                                             f64, i32, P, i64, P, P]
+    lib.oracle_attention_variant.restype = i32
     lib.oracle_prefill_paged.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64,
                                          i32, i32, f64, i32, P, i64, P, P]
     lib.oracle_prefill_paged.restype = i32
@@ -135,6 +138,28 @@ def attention(q, k, v, causal: bool, scale: float, dtype: int, rows=None, return
         if P is not None:
             P = P.reshape(B, Hq, N, N)
     return (O, L, P) if return_probs else (O, L)
+
+
+def attention_variant(q, k, v, causal: bool, window: int, softcap: float, scale: float,
+                      dtype: int, rows=None):
+    """Attention with a sliding window (window > 0, causal only) and/or logits soft-cap
+    (softcap > 0).  Layouts and returns as attention()."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == k.shape
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = B * Hq * N if r is None else len(r)
+    O = np.zeros((n, d), dtype=np.float64)
+    L = np.zeros(n, dtype=np.float64)
+    rc = _L().oracle_attention_variant(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d,
+                                       int(bool(causal)), int(window), float(softcap),
+                                       float(scale), int(dtype), _ptr(r), n, _ptr(O), _ptr(L))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_variant rejected its arguments ({rc})")
+    if rows is None:
+        O, L = O.reshape(B, Hq, N, d), L.reshape(B, Hq, N)
+    return O, L
 
 
 def decode_paged(q, k_pages, v_pages, block_table, ctx_lens, scale: float, dtype: int,

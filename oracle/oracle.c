@@ -17,6 +17,11 @@
  *                        handbook "FlashAttention and inference operators", causal masking].
  *                        GQA maps query head h to kv head h / (Hq/Hkv) [same handbook,
  *                        paged decode kernel].
+ *   oracle_attention_variant  Standard attention with two of the variants a template engine
+ *                        supports [CS349D Lecture 4 notes 5.4]: logits soft-cap, where each
+ *                        scaled score s becomes c * tanh(s / c) before the softmax, and a
+ *                        sliding window, where query i sees only its last w keys
+ *                        (i - w < j <= i).  Otherwise as oracle_attention.
  *   oracle_decode_paged  One query per request over a paged KV cache: token t of request r
  *                        lives in physical page block_table[r][t / page] at slot t % page
  *                        [handbook, PagedAttention section; LLM Internals 10.3.7].  All ctx
@@ -178,6 +183,77 @@ int oracle_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, in
             }
         }
         free(s); free(q); free(tmp); free(kr); free(vr); free(prow);
+    }
+    return err ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ attention variants
+ * As oracle_attention (same layouts, rows, outputs), with
+ *   window  > 0: query i sees keys max(0, i - window + 1) .. i (requires causal); 0 = off;
+ *   softcap > 0: each scaled score s = scale * q.k becomes softcap * tanh(s / softcap)
+ *                before the softmax (and so in LSE); 0 = off.
+ * Returns 0, or -1 on bad arguments / allocation failure.                                   */
+int oracle_attention_variant(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B,
+                             int Hq, int Hkv, int N, int d, int causal, int window,
+                             double softcap, double scale, int dtype, const int64_t* rows,
+                             int64_t n_rows, double* O, double* LSE)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || Hq % Hkv) return -1;
+    if (window < 0 || (window > 0 && !causal) || softcap < 0.0) return -1;
+    const int64_t total = (int64_t)B * Hq * N;
+    if (!rows) n_rows = total;
+    const int group = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+        double* q = (double*)malloc(sizeof(double) * (size_t)d);
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+        const int ok = s && q && tmp;
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < n_rows; ++t) {
+            int64_t r = rows ? rows[t] : t;
+            if (!ok || r < 0 || r >= total) {
+#pragma omp atomic write
+                err = 1;
+                continue;
+            }
+            int i = (int)(r % N);
+            int h = (int)((r / N) % Hq);
+            int b = (int)(r / ((int64_t)N * Hq));
+            int kvh = h / group;
+            const uint16_t* kbase = K + ((int64_t)b * Hkv + kvh) * N * d;
+            const uint16_t* vbase = V + ((int64_t)b * Hkv + kvh) * N * d;
+            int hi = causal ? i + 1 : N;                            /* keys j < hi ...      */
+            int lo = window > 0 && i - window + 1 > 0 ? i - window + 1 : 0;   /* ... j >= lo */
+            int n = hi - lo;
+            double* out = O + t * d;
+            for (int c = 0; c < d; ++c) out[c] = 0.0;
+            widen_row(Q + r * d, d, dtype, q);
+            /* scores of the visible keys, soft-capped if asked */
+            for (int j = 0; j < n; ++j) {
+                widen_row(kbase + (int64_t)(lo + j) * d, d, dtype, tmp);
+                double acc = 0.0;
+                for (int k = 0; k < d; ++k) acc += q[k] * tmp[k];
+                s[j] = scale * acc;
+                if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);
+            }
+            /* safe softmax over the visible keys, then O = P V and LSE = m + ln l */
+            double m = s[0];
+            for (int j = 1; j < n; ++j)
+                if (s[j] > m) m = s[j];
+            double l = 0.0;
+            for (int j = 0; j < n; ++j) {
+                s[j] = exp(s[j] - m);
+                l += s[j];
+            }
+            for (int j = 0; j < n; ++j) {
+                widen_row(vbase + (int64_t)(lo + j) * d, d, dtype, tmp);
+                for (int c = 0; c < d; ++c) out[c] += (s[j] / l) * tmp[c];
+            }
+            LSE[t] = m + log(l);
+        }
+        free(s); free(q); free(tmp);
     }
     return err ? -1 : 0;
 }

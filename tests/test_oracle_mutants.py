@@ -23,7 +23,7 @@ MUTANTS = {
                            "int kvh = h % Hkv;\n                const uint16_t* kbase"),
     "k_and_v_swapped": ("kr[j] = kbase + (int64_t)j * d;\n                    vr[j] = vbase",
                         "kr[j] = vbase + (int64_t)j * d;\n                    vr[j] = kbase"),
-    "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "scale_dropped": ("        s[j] = scale * acc;\n    }", "        s[j] = acc;\n    }"),
     "merge_weight_inverted": ("double w = exp(lse_s[s] - M);", "double w = exp(M - lse_s[s]);"),
     "decode_wrong_slot": ("int slot = tok % page_size;", "int slot = (tok + 1) % page_size;"),
     "fp16_wrong_bias": ("expo - 25);", "expo - 24);"),
@@ -38,6 +38,12 @@ MUTANTS = {
     "paged_prefill_row_not_rebased": ("int i = tok - cu_seqlens_q[r];", "int i = tok;"),
     "paged_prefill_wrong_kv_slot": ("int in_page = key % page_size;",
                                     "int in_page = (key + 1) % page_size;"),
+    "window_one_key_too_many": ("int lo = window > 0 && i - window + 1 > 0 ? i - window + 1 : 0;",
+                                "int lo = window > 0 && i - window > 0 ? i - window : 0;"),
+    "softcap_without_inner_division": ("if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);",
+                                       "if (softcap > 0.0) s[j] = softcap * tanh(s[j]);"),
+    "softcap_before_scale": ("s[j] = scale * acc;\n                if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);",
+                             "s[j] = acc;\n                if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);\n                s[j] *= scale;"),
 }
 
 PINS = [
@@ -56,6 +62,9 @@ PINS = [
     pins.test_decode_matches_torch_sdpa_and_is_page_order_free,
     pins.test_cascade_matches_torch_sdpa_over_prefix_then_own_tokens,
     lambda: pins.test_paged_prefill_matches_torch_sdpa_bottom_right(True),
+    lambda: pins.test_sliding_window_matches_torch_sdpa_with_its_own_mask(5, pins.BF16),
+    pins.test_softcap_tends_to_plain_attention_as_the_cap_grows,
+    pins.test_softcap_bounds_the_weight_ratio_and_follows_the_scale,
 ]
 
 

@@ -531,3 +531,76 @@ def test_paged_prefill_rejects_padding_rows_and_handles_short_caches():
                                 case.cu_seqlens_q, case.kv_lens, True, case.scale, BF16)
     assert np.all(L[:2] == -np.inf) and np.all(O[:2] == 0.0)
     assert np.all(np.isfinite(L[2:]))
+
+
+# ----------------------------------------------------------------------------- variants
+# [CS349D Lecture 4 notes 5.4] logits soft-cap s -> c tanh(s / c) and a sliding window where
+# each query sees its last w keys.
+
+@pytest.mark.parametrize("window,dtype", [(1, BF16), (5, BF16), (16, FP16), (33, BF16), (200, BF16)])
+def test_sliding_window_matches_torch_sdpa_with_its_own_mask(window, dtype):
+    c = prefill_case(2, 4, 2, 70, 16, True, dtype, seeds=(101, 102, 103))
+    O, L = oracle.attention_variant(c.q, c.k, c.v, True, window, 0.0, c.scale, dtype)
+    i = np.arange(70)
+    mask = torch.from_numpy((i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - window))
+    q, k, v = (torch.from_numpy(bits_to_f64(x, dtype)) for x in (c.q, c.k, c.v))
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=c.scale, enable_gqa=True)
+    np.testing.assert_allclose(O, o.numpy(), rtol=1e-12, atol=1e-12)
+    s = c.scale * np.einsum("bhid,bhjd->bhij", q.numpy(), np.repeat(k.numpy(), 2, axis=1))
+    s = np.where(mask.numpy(), s, -np.inf)
+    np.testing.assert_allclose(L, sps.logsumexp(s, axis=-1), rtol=1e-12, atol=1e-12)
+
+
+def test_sliding_window_closed_forms():
+    c = prefill_case(1, 2, 1, 40, 8, True, BF16, seeds=(104, 105, 106))
+    # a window of one key: each row returns its own V row exactly
+    O, L = oracle.attention_variant(c.q, c.k, c.v, True, 1, 0.0, c.scale, BF16)
+    assert np.array_equal(O[0, :, :, :], np.repeat(bits_to_f64(c.v, BF16)[0], 2, axis=0))
+    # a window as long as the sequence is plain causal attention
+    O2, L2 = oracle.attention_variant(c.q, c.k, c.v, True, 40, 0.0, c.scale, BF16)
+    O3, L3 = oracle.attention(c.q, c.k, c.v, True, c.scale, BF16)
+    np.testing.assert_allclose(O2, O3, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(L2, L3, rtol=1e-14, atol=1e-14)
+    # zero queries: LSE counts the keys in the window
+    q0 = np.zeros_like(c.q)
+    _, L0 = oracle.attention_variant(q0, c.k, c.v, True, 7, 0.0, c.scale, BF16)
+    want = np.log(np.minimum(np.arange(40) + 1, 7))
+    np.testing.assert_allclose(L0[0, 0], want, rtol=0, atol=1e-14)
+    with pytest.raises(ValueError):
+        oracle.attention_variant(c.q, c.k, c.v, False, 7, 0.0, c.scale, BF16)
+
+
+def test_softcap_tends_to_plain_attention_as_the_cap_grows():
+    c = prefill_case(1, 4, 2, 50, 16, True, BF16, seeds=(107, 108, 109))
+    q, k, v = (torch.from_numpy(bits_to_f64(x, BF16)) for x in (c.q, c.k, c.v))
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=c.scale,
+                                       enable_gqa=True).numpy()
+    O, _ = oracle.attention_variant(c.q, c.k, c.v, True, 0, 1e30, c.scale, BF16)
+    np.testing.assert_allclose(O, o, rtol=1e-12, atol=1e-12)
+    # c tanh(s / c) = s - s^3 / (3 c^2) + ...: the distance to plain attention falls as 1 / c^2
+    e1 = np.abs(oracle.attention_variant(c.q, c.k, c.v, True, 0, 20.0, c.scale, BF16)[0] - o).max()
+    e2 = np.abs(oracle.attention_variant(c.q, c.k, c.v, True, 0, 40.0, c.scale, BF16)[0] - o).max()
+    assert 0.2 < e2 / e1 < 0.3, (e1, e2)
+
+
+def test_softcap_bounds_the_weight_ratio_and_follows_the_scale():
+    # V = identity (d = N) makes each output row the row of weights P; capped scores lie in
+    # (-c, c), so no two weights differ by more than e^(2c), and large scores reach it
+    N, cap = 16, 1.5
+    rng = np.random.default_rng(110)
+    qf = np.full((1, 1, N, N), 1.0, np.float32)
+    kf = np.zeros((1, 1, N, N), np.float32)
+    kf[0, 0, :, 0] = np.where(rng.random(N) < 0.5, 64.0, -64.0)   # scores +-64
+    kf[0, 0, 0, 0], kf[0, 0, 1, 0] = 64.0, -64.0
+    vf = np.eye(N, dtype=np.float32)[None, None]
+    qb, kb, vb = (f32_to_bf16_bits(x) for x in (qf, kf, vf))
+    P, _ = oracle.attention_variant(qb, kb, vb, False, 0, cap, 1.0, BF16)
+    ratio = P[0, 0].max(axis=1) / P[0, 0].min(axis=1)
+    assert np.all(ratio <= np.exp(2 * cap) * (1 + 1e-12)) and np.all(ratio > 0.999 * np.exp(2 * cap))
+    # the cap applies to the scaled score: scale 2 on q equals q doubled (exact in bf16)
+    c = prefill_case(1, 2, 2, 30, 8, True, BF16, seeds=(111, 112, 113))
+    q2 = f32_to_bf16_bits(2.0 * bits_to_f64(c.q, BF16).astype(np.float32))
+    Oa, La = oracle.attention_variant(c.q, c.k, c.v, True, 0, 3.0, 2.0, BF16)
+    Ob, Lb = oracle.attention_variant(q2, c.k, c.v, True, 0, 3.0, 1.0, BF16)
+    np.testing.assert_allclose(Oa, Ob, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(La, Lb, rtol=1e-14, atol=1e-14)
