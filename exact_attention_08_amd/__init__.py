@@ -61,6 +61,8 @@ _lib.attn_decode_cascade.argtypes = [_P, _P, _P, _i, _P, _P, _P, _P, _P, _P, _i,
 _lib.attn_decode_cascade.restype = _i
 _lib.attn_decode_cascade_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.attn_decode_cascade_workspace_bytes.restype = _sz
+_lib.attn_fwd_variant.argtypes = [_P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i, _f, _f, _i, _P]
+_lib.attn_fwd_variant.restype = _i
 _lib.attn_prefill_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i,
                                     _i, _f, _i, _P]
 _lib.attn_prefill_paged.restype = _i
@@ -71,7 +73,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -7: "ATTN_ERR_HIP"}
 ATTN_BF16, ATTN_FP16 = 0, 1
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
-           "attn_decode_cascade", "attn_decode_cascade_workspace_bytes", "attn_prefill_paged")
+           "attn_decode_cascade", "attn_decode_cascade_workspace_bytes", "attn_prefill_paged",
+           "attn_fwd_variant")
 
 
 class AttnError(RuntimeError):
@@ -128,6 +131,29 @@ def attn_fwd(Q, K, V, O, LSE, causal: bool, scale: float | None = None, stream=N
                          B, Hq, K.shape[1], N, d, int(bool(causal)), float(scale), dt,
                          _stream_ptr(Q, stream))
     _check("attn_fwd", code)
+
+
+def attn_fwd_variant(Q, K, V, O, LSE, causal: bool, window: int = 0, softcap: float = 0.0,
+                     scale: float | None = None, stream=None) -> None:
+    """As attn_fwd, with a causal sliding window (window > 0: query i sees keys
+    i - window < j <= i) and/or logits soft-cap (softcap > 0: s -> c tanh(s / c))."""
+    import torch
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("LSE", LSE)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(Q.dim() == 4 and K.dim() == 4 and V.shape == K.shape and O.shape == Q.shape,
+          "Q,O must be [B,Hq,N,d] and K,V [B,Hkv,N,d]")
+    B, Hq, N, d = Q.shape
+    _need(K.shape[0] == B and K.shape[2] == N and K.shape[3] == d, "K/V shape mismatch")
+    _need(LSE.dtype == torch.float32 and tuple(LSE.shape) == (B, Hq, N), "LSE must be fp32 [B,Hq,N]")
+    dt = _dtype_code(Q)
+    _need(K.dtype == Q.dtype and V.dtype == Q.dtype and O.dtype == Q.dtype, "dtypes must match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _lib.attn_fwd_variant(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                 LSE.data_ptr(), B, Hq, K.shape[1], N, d, int(bool(causal)),
+                                 int(window), float(softcap), float(scale), dt,
+                                 _stream_ptr(Q, stream))
+    _check("attn_fwd_variant", code)
 
 
 def attn_decode_paged_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq,

@@ -57,6 +57,27 @@ extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, fl
     return attn::launch_prefill(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+extern "C" int attn_fwd_variant(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                                float softcap, float scale, int dtype, void* stream) {
+    if (!Q || !K || !V || !O || !LSE) return ATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SHAPE;
+    if (window < 0 || !(softcap >= 0.f) || !isfinite(softcap)) return ATTN_ERR_SHAPE;
+    if ((long long)B * Hq * (long long)N * d > (1LL << 46)) return ATTN_ERR_SHAPE;
+    if ((long long)N * d * 2 > (1LL << 30)) return ATTN_ERR_SHAPE;
+    if ((long long)((N + 127) / 128) * B * Hq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;   // the sliding window is causal
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+        !aligned(LSE, 16))
+        return ATTN_ERR_ALIGN;
+    attn::PrefillArgs a{Q, K, V, O, LSE, B, Hq, Hkv, N, d, causal != 0, dtype == ATTN_BF16,
+                        scale, stream};
+    return attn::launch_prefill_variant(a, window, softcap) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int page_size,
                                                     int max_pages_per_seq, int split_tokens) {
     if (B <= 0 || Hq <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||

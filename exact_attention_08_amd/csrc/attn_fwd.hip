@@ -127,7 +127,18 @@ struct ModeGeo {
     int n_chunks;
     int s_stride;   // partial states per (request, query head)
     int s_base;     // index of the first prefix chunk among them
+    // variants (FEAT): sliding window length; soft-cap constants 2 log2(e) scale / c and
+    // c / scale (a raw score s becomes (c / scale) tanh(s scale / c))
+    int window;
+    float cap_in, cap_out;
 };
+
+// Variants of dense attention [CS349D Lecture 4 notes 5.4]: kFeatWindow -- query i sees only
+// keys i - window < j <= i (causal); kFeatCap -- each scaled score s becomes c tanh(s / c)
+// before the softmax.  An item then starts at the tile holding its first visible key, each
+// wave skips the blocks left of its rows' windows, and the capped scores replace the raw
+// ones before the masks, the maximum and the exponentials.
+enum { kFeatWindow = 1, kFeatCap = 2 };
 
 // Paged / varlen prefill [LLM Internals 10.3.8, variable-length batching; 10.3.7, block
 // table; CS349D Lecture 4 section 5.1, incremental prefill].  Request r's new queries are
@@ -144,7 +155,7 @@ enum { kModeDense = 0, kModePrefix = 1, kModePaged = 2 };
 // prefix [Hkv, N, d], O (as fp32) and LSE the partial-state buffers.  kModePaged: Q is q
 // [total_q, Hq, d], K/V the page pools [pages, 16, Hkv, d], O [total_q, Hq, d], LSE
 // [total_q, Hq] or null.
-template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST, int MODE>
+template <int D, bool IS_BF16, bool CAUSAL, bool PERSIST, int MODE, int FEAT = 0>
 __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -153,6 +164,10 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     const int* __restrict__ pg_kv_lens, int pg_max_pages) {
     constexpr bool CASC = MODE == kModePrefix;
     constexpr bool PAGED = MODE == kModePaged;
+    constexpr bool WIN = (FEAT & kFeatWindow) != 0;
+    constexpr bool CAP = (FEAT & kFeatCap) != 0;
+    static_assert(FEAT == 0 || (MODE == kModeDense && !PERSIST), "variants: dense, one item per workgroup");
+    static_assert(!WIN || CAUSAL, "the sliding window is causal");
     static_assert(!CASC || (!CAUSAL && !PERSIST), "the prefix mode is non-causal, one item per workgroup");
     static_assert(!PAGED || !PERSIST, "the paged mode runs one item per workgroup");
     using E = Elem<IS_BF16>;
@@ -252,7 +267,9 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         // Keys of the item: [kbase, kend) (a prefix chunk, the request's cache, or the whole
         // sequence).  KV tiles this workgroup visits: causal stops after the block holding
         // its last row.
-        const int kbase = CASC ? chunk_id * cg.chunk : 0;
+        // window: the item starts at the tile holding the first key its first row sees
+        const int kbase = CASC ? chunk_id * cg.chunk
+                        : WIN ? (max(0, q_tile0 - cg.window + 1) / BC) * BC : 0;
         const int kend = CASC ? min(N, kbase + cg.chunk) : PAGED ? pkv_len : N;
         // paged: row t is query t / G at position pq_pos0 + t / G
         const int pq_pos0 = pkv_len - pq_len;
@@ -265,6 +282,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             kv_last = CAUSAL ? min(N, q_tile0 + kBR) - 1 : kend - 1;
             n_kv = (kv_last - kbase) / BC + 1;
         }
+        (void)pq_pos0;
         const int wave_last_q = min(q0w + 32 * kQB - 1, n_qrows - 1);
 
         // a2: this lane's Q rows (one per column block) as the B operand of S^T = K Q^T
@@ -371,8 +389,12 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) qpos[qb] = pq_pos0 + (q0w + 32 * qb + l32) / G;
         } else {
-            nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, wave_last_q / 32 + 1) : nb);
+            nb_live = !wave_live ? 0 : (CAUSAL ? min(nb, (wave_last_q - kbase) / 32 + 1) : nb);
         }
+        // window: the wave's first block holding a key its first row sees, and the largest
+        // left edge among its rows (blocks starting before it need the elementwise mask)
+        const int nb_first = WIN ? max(0, q0w - cg.window + 1 - kbase) / 32 : 0;
+        const int win_lo_max = WIN ? wave_last_q - cg.window + 1 : 0;
 
         // V^T operand of the second product from V (rows in key order) with the transposing LDS read
         // (ds_read_b64_tr_b16): within each 16-lane group G, destination lane i receives, as
@@ -426,7 +448,10 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             constexpr int ST = decltype(stage)::value;   // == j & 1
             const int bi = j * NKB + kb;
             const int kfirst = kbase + bi * 32;
-            const bool live = bi < nb_live;            // wave-uniform
+            // live: the wave computes this block; need_next: it computes the next block's S^T
+            // here (with a window, also in the block just before its first live one)
+            const bool live = WIN ? (bi >= nb_first && bi < nb_live) : bi < nb_live;   // wave-uniform
+            const bool need_next = WIN ? (bi + 1 >= nb_first && bi < nb_live) : live;
             u32x4 va[2][NDB];
             u32x4 ka[NKS];
             float m_use[kQB];
@@ -441,10 +466,21 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                         const u32x2 hi = read_tr(vp + 8 * RB);
                         va[h][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                     }
-                if (kb + 1 < NKB) read_k(ka, ST, kb + 1);
+                if (!WIN && kb + 1 < NKB) read_k(ka, ST, kb + 1);
                 // 2. statistics
+                if constexpr (CAP) {
+                    // soft-cap: s -> (c / scale) tanh(s scale / c), tanh(y) = 1 - 2 / (1 + e^2y)
+    #pragma unroll
+                    for (int qb = 0; qb < kQB; ++qb)
+    #pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const float e = fast_exp2(sc[qb][v] * cg.cap_in);
+                            const float r = __builtin_amdgcn_rcpf(1.f + e);
+                            sc[qb][v] = __builtin_fmaf(-2.f * cg.cap_out, r, cg.cap_out);
+                        }
+                }
                 const bool mask_blk = (CAUSAL && kfirst + 31 > (PAGED ? pos_first : q0w)) ||
-                                      kfirst + 32 > kend;
+                                      kfirst + 32 > kend || (WIN && kfirst < win_lo_max);
     #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
                     // a5: elementwise mask (select, never multiply)
@@ -453,7 +489,8 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     #pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const int key = kfirst + 8 * (v >> 2) + 4 * g + (v & 3);
-                            const bool masked = key >= kend || (CAUSAL && key > q);
+                            const bool masked = key >= kend || (CAUSAL && key > q) ||
+                                                (WIN && key < q - cg.window + 1);
                             sc[qb][v] = masked ? -INFINITY : sc[qb][v];
                         }
                     }
@@ -468,9 +505,9 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                         const float m_blk = fmaxf(mloc, xor_lanes(mloc, 32)) * scale_log2;
                         const bool move = m_blk > m_ref[qb] + kRescaleSlack;
                         const float m_new = move ? m_blk : m_ref[qb];
-                        // 0 on the first block; a paged row that has seen no key yet
-                        // (reference still -inf) keeps alpha = 1
-                        const float alpha = (PAGED && m_new == -INFINITY)
+                        // 0 on the first block; a row that has seen no key yet (paged, or
+                        // left of a window; reference still -inf) keeps alpha = 1
+                        const float alpha = ((PAGED || WIN) && m_new == -INFINITY)
                                                 ? 1.f : fast_exp2(m_ref[qb] - m_new);
                         l_run[qb] *= alpha;
     #pragma unroll
@@ -487,11 +524,18 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 wait_tile();
                 __syncthreads();
                 if (j + 2 < n_kv) dma_tile(j + 2, ST);
-                if (live) read_k(ka, 1 - ST, 0);
+                if (need_next) read_k(ka, 1 - ST, 0);
             }
-            // 4. next S^T, this block's weights and O^T update
+            if constexpr (WIN) {
+                if (need_next && kb + 1 < NKB) read_k(ka, ST, kb + 1);
+            }
+            // 4. next S^T, this block's weights and O^T update (with a window the next
+            // S^T may be due in a block that is not live itself)
+            if constexpr (WIN) {
+                if (need_next) s_product(ka, sn);
+            }
             if (live) {
-                s_product(ka, sn);
+                if constexpr (!WIN) s_product(ka, sn);
     #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
                     float p[16];
@@ -524,7 +568,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
 
         static_assert(NKB == 2, "the block loop alternates two score buffers over two blocks per tile");
         f32x16 s_a[kQB], s_b[kQB];
-        if (nb_live > 0) {
+        if (nb_live > 0 && nb_first == 0) {
             u32x4 ka[NKS];
             read_k(ka, 0, 0);
             s_product(ka, s_a);
@@ -632,6 +676,36 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
                          nullptr, nullptr, 0);
 }
 
+template <int D, bool IS_BF16, bool CAUSAL, int FEAT>
+hipError_t launch_variant_t(const PrefillArgs& a, int window, float softcap) {
+    constexpr int kBR = 32 * PrefillTile<D>::QB * kWaves;
+    const int n_qtiles = (a.N + kBR - 1) / kBR;
+    const int n_hg = a.B * a.Hkv;
+    const long long n_items = (long long)n_qtiles * a.B * a.Hq;
+    const int xcd_major = (n_hg % 8 == 0) ? 1 : 0;
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    ModeGeo cg{};
+    cg.window = window;
+    if (softcap > 0.f) {
+        cg.cap_in = (float)(2.0 * 1.4426950408889634 * (double)a.scale / (double)softcap);
+        cg.cap_out = (float)((double)softcap / (double)a.scale);
+    }
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, kModeDense, FEAT>,
+                         dim3((unsigned)n_items), dim3(kThreads), (hipStream_t)a.stream,
+                         "prefill_fwd_kernel(variant)", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq,
+                         a.Hkv, a.N, scale_log2, n_qtiles, (int)n_items, xcd_major, cg, nullptr,
+                         nullptr, nullptr, 0);
+}
+
+template <int D, bool IS_BF16>
+hipError_t launch_variant_d(const PrefillArgs& a, int window, float softcap) {
+    const bool cap = softcap > 0.f;
+    if (!a.causal) return launch_variant_t<D, IS_BF16, false, kFeatCap>(a, 0, softcap);
+    if (window > 0 && cap) return launch_variant_t<D, IS_BF16, true, kFeatWindow | kFeatCap>(a, window, softcap);
+    if (window > 0) return launch_variant_t<D, IS_BF16, true, kFeatWindow>(a, window, 0.f);
+    return launch_variant_t<D, IS_BF16, true, kFeatCap>(a, 0, softcap);
+}
+
 template <int D, bool IS_BF16>
 hipError_t launch_cascade_prefix_t(const CascadePrefixArgs& a) {
     constexpr int kBR = 32 * PrefillTile<D>::QB * kWaves;
@@ -678,6 +752,14 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.is_bf16) return a.causal ? launch_prefill_t<64, true, true>(a)
                                    : launch_prefill_t<64, true, false>(a);
     return a.causal ? launch_prefill_t<64, false, true>(a) : launch_prefill_t<64, false, false>(a);
+}
+
+hipError_t launch_prefill_variant(const PrefillArgs& a, int window, float softcap) {
+    if (window <= 0 && !(softcap > 0.f)) return launch_prefill(a);   // plain attention
+    if (a.d == 128) return a.is_bf16 ? launch_variant_d<128, true>(a, window, softcap)
+                                     : launch_variant_d<128, false>(a, window, softcap);
+    return a.is_bf16 ? launch_variant_d<64, true>(a, window, softcap)
+                     : launch_variant_d<64, false>(a, window, softcap);
 }
 
 hipError_t launch_prefill_paged(const PagedPrefillArgs& a) {

@@ -100,6 +100,9 @@ hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_cascade_prefix(const CascadePrefixArgs& a);
 hipError_t launch_prefill_paged(const PagedPrefillArgs& a);
+// dense attention with a causal sliding window (window > 0) and/or logits soft-cap
+// (softcap > 0); both off is plain launch_prefill
+hipError_t launch_prefill_variant(const PrefillArgs& a, int window, float softcap);
 
 // Prefix keys per partial state in a cascade decode.
 constexpr int kCascadeChunk = 512;

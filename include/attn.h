@@ -19,6 +19,8 @@
  *   attn_decode_cascade  decode for requests that share a prefix: the prefix is read once for
  *                      all of them, then merged with each request's own tokens by the LSE
  *                      rule [CS349D Lecture 4 notes 4.4, 5.3]
+ *   attn_fwd_variant   attn_fwd with a causal sliding window and/or logits soft-cap
+ *                      [CS349D Lecture 4 notes 5.4, attention variants]
  *   attn_prefill_paged  prefill of a chunk of new tokens per request over its paged KV
  *                      cache, requests packed end to end by cumulative lengths
  *                      [LLM Internals 10.3.8 variable-length batching, 10.3.7 block table;
@@ -91,6 +93,22 @@ enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
              int dtype, void* stream);
+
+/*
+ * attn_fwd_variant -- attn_fwd with two attention variants [CS349D Lecture 4 notes 5.4]:
+ *   window  > 0: sliding window (causal only): query i sees keys j with i - window < j <= i;
+ *                0 = off
+ *   softcap > 0: logits soft-cap: each scaled score s = scale * q.k becomes
+ *                softcap * tanh(s / softcap) before the softmax (and in LSE); 0 = off
+ * Both off is exactly attn_fwd.  Arguments, layouts and the rest as attn_fwd.
+ *
+ *   Supported: as attn_fwd; window > 0 requires causal (else ATTN_ERR_UNSUPPORTED);
+ *   window < 0 or softcap < 0 or not finite is ATTN_ERR_SHAPE.  Returns ATTN_OK or a
+ *   negative attn_status.
+ */
+int attn_fwd_variant(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                     float softcap, float scale, int dtype, void* stream);
 
 /*
  * attn_prefill_paged -- prefill of new tokens over a paged KV cache (chunked prefill)

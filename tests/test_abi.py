@@ -175,3 +175,21 @@ def test_balanced_split_workspace_is_sized_for_the_shortest_split():
     small = ws(2, 8, 128, 16, 64, 1024)
     assert small < ws(2, 8, 128, 16, 64, 0)
     assert dec(split=0, max_pages=64, ws_bytes=small) == -6
+
+
+def fvar(Q=A, K=A, V=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, N=100, d=128, causal=1, window=16,
+         softcap=30.0, scale=0.1, dtype=0):
+    return L.attn_fwd_variant(Q, K, V, O, LSE, B, Hq, Hkv, N, d, causal, window, softcap,
+                              scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), -1), (dict(LSE=None), -1),
+    (dict(B=0), -2), (dict(Hq=7), -2), (dict(window=-1), -2), (dict(softcap=-1.0), -2),
+    (dict(softcap=float("inf")), -2), (dict(scale=0.0), -2),
+    (dict(dtype=4), -3),
+    (dict(d=96), -4), (dict(causal=0), -4),
+    (dict(Q=MIS), -5), (dict(O=MIS), -5),
+])
+def test_attn_fwd_variant_rejects_bad_arguments(kw, code):
+    assert fvar(**kw) == code
