@@ -16,7 +16,8 @@ every K/V element of every context read once, plus q, O, block table and lengths
 times the fp64 CPU oracle on a bounded sample of the same workloads.  Outside the step
 (skipped with --no-extra): the Llama-3-8B prefill shapes, the shared-prefix decode
 (attn_decode_cascade) next to the same requests through attn_decode_paged, and chunked
-prefill over a paged cache (attn_prefill_paged), and the read bandwidth a plain streaming
+prefill over a paged cache (attn_prefill_paged), the sliding-window + soft-cap prefill
+(attn_fwd_variant), and the read bandwidth a plain streaming
 kernel reaches (the practical HBM ceiling).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--cpu-seconds 10] [--no-extra]
@@ -120,6 +121,49 @@ def paged_prefill_figure(attn, torch, dev, log, reps=10):
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
                          "kernel": "prefill_fwd_kernel<128,bf16,causal,paged>"},
             "total_q": c.total_q, "total_kv": int(c.kv_lens.astype("int64").sum())}
+
+
+VARIANT = dict(name="llama3_8b_prefill_n8192_window4096_softcap50", B=1, Hq=32, Hkv=8,
+               N=8192, d=128, window=4096, softcap=50.0)
+
+
+def variant_flops(v):
+    """Algorithmic FLOPs of causal attention with a sliding window: 4 * d per visible
+    (query, key) pair; query i sees min(i + 1, window) keys."""
+    i = __import__("numpy").arange(v["N"], dtype="int64")
+    pairs = int(__import__("numpy").minimum(i + 1, v["window"]).sum())
+    return 4.0 * v["B"] * v["Hq"] * v["d"] * pairs
+
+
+def variant_figure(attn, torch, dev, log, reps=10):
+    """attn_fwd_variant at Llama-3-8B heads with a 4096-key window and soft-cap 50."""
+    from attn_inputs import prefill_case
+    v = VARIANT
+    log(f"bench: extra figure {v['name']}")
+    c = prefill_case(v["B"], v["Hq"], v["Hkv"], v["N"], v["d"], True)
+    Q, K, V = (to_dev(x, c.dtype) for x in (c.q, c.k, c.v))
+    O = torch.empty_like(Q)
+    L = torch.empty(v["B"], v["Hq"], v["N"], dtype=torch.float32, device=dev)
+
+    def call():
+        attn.attn_fwd_variant(Q, K, V, O, L, True, v["window"], v["softcap"], c.scale)
+
+    for _ in range(2):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    assert torch.isfinite(L).all()
+    tf = variant_flops(v) / t / 1e12
+    return {"workload": v["name"], "avg_launch_us": round(t * 1e6, 1),
+            "algorithmic_flops_per_launch": variant_flops(v),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                         "kernel": "prefill_fwd_kernel<128,bf16,causal,window+softcap>"}}
 
 
 def hbm_read_ceiling(torch, dev, log, gib=2, reps=5):
@@ -458,10 +502,11 @@ def main():
             del Qx, Kx, Vx, Ox, Lx
             torch.cuda.empty_cache()
 
-    casc = ppre = ceil = None
+    casc = ppre = ceil = var = None
     if not args.no_extra and args.only is None:
         casc = cascade_figure(attn, torch, dev, log)
         ppre = paged_prefill_figure(attn, torch, dev, log)
+        var = variant_figure(attn, torch, dev, log)
         ceil = hbm_read_ceiling(torch, dev, log)
 
     cpu = None
@@ -496,6 +541,7 @@ def main():
         "cascade_decode": casc,
         "hbm_read_ceiling": ceil,
         "paged_prefill": ppre,
+        "prefill_variant": var,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     constexpr bool PAGED = MODE == kModePaged;
     constexpr bool WIN = (FEAT & kFeatWindow) != 0;
     constexpr bool CAP = (FEAT & kFeatCap) != 0;
-    static_assert(FEAT == 0 || (MODE == kModeDense && !PERSIST), "variants: dense, one item per workgroup");
+    static_assert(FEAT == 0 || MODE == kModeDense, "variants of dense attention");
     static_assert(!WIN || CAUSAL, "the sliding window is causal");
     static_assert(!CASC || (!CAUSAL && !PERSIST), "the prefix mode is non-causal, one item per workgroup");
     static_assert(!PAGED || !PERSIST, "the paged mode runs one item per workgroup");
@@ -529,13 +529,13 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             if constexpr (WIN) {
                 if (need_next && kb + 1 < NKB) read_k(ka, ST, kb + 1);
             }
-            // 4. next S^T, this block's weights and O^T update (with a window the next
-            // S^T may be due in a block that is not live itself)
+            // 4. next S^T, this block's weights and O^T update (a live block always needs
+            // the next S^T; with a window, so does the block just before the first live one)
             if constexpr (WIN) {
-                if (need_next) s_product(ka, sn);
+                if (!live && need_next) s_product(ka, sn);
             }
             if (live) {
-                if constexpr (!WIN) s_product(ka, sn);
+                s_product(ka, sn);
     #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
                     float p[16];
@@ -645,8 +645,8 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     }
 }
 
-template <int D, bool IS_BF16, bool CAUSAL>
-hipError_t launch_prefill_t(const PrefillArgs& a) {
+template <int D, bool IS_BF16, bool CAUSAL, int FEAT = 0>
+hipError_t launch_prefill_t(const PrefillArgs& a, const ModeGeo& cg = ModeGeo{}) {
     constexpr int kBR = 32 * PrefillTile<D>::QB * kWaves;
     const int n_qtiles = (a.N + kBR - 1) / kBR;
     const int n_hg = a.B * a.Hkv;
@@ -664,37 +664,28 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     const long long grid = persistent && n_items > slots ? slots : n_items;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     if (grid < n_items)
-        return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, true, kModeDense>,
+        return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, true, kModeDense, FEAT>,
                              dim3((unsigned)grid), dim3(kThreads), (hipStream_t)a.stream,
                              "prefill_fwd_kernel", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv,
-                             a.N, scale_log2, n_qtiles, (int)n_items, xcd_major, ModeGeo{},
+                             a.N, scale_log2, n_qtiles, (int)n_items, xcd_major, cg,
                              nullptr, nullptr, nullptr, 0);
-    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, kModeDense>,
+    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, kModeDense, FEAT>,
                          dim3((unsigned)grid), dim3(kThreads), (hipStream_t)a.stream,
                          "prefill_fwd_kernel", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq, a.Hkv, a.N,
-                         scale_log2, n_qtiles, (int)n_items, xcd_major, ModeGeo{}, nullptr,
+                         scale_log2, n_qtiles, (int)n_items, xcd_major, cg, nullptr,
                          nullptr, nullptr, 0);
 }
 
+// Variants share the dense launch (grid choice included); only the item geometry differs.
 template <int D, bool IS_BF16, bool CAUSAL, int FEAT>
 hipError_t launch_variant_t(const PrefillArgs& a, int window, float softcap) {
-    constexpr int kBR = 32 * PrefillTile<D>::QB * kWaves;
-    const int n_qtiles = (a.N + kBR - 1) / kBR;
-    const int n_hg = a.B * a.Hkv;
-    const long long n_items = (long long)n_qtiles * a.B * a.Hq;
-    const int xcd_major = (n_hg % 8 == 0) ? 1 : 0;
-    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     ModeGeo cg{};
     cg.window = window;
     if (softcap > 0.f) {
         cg.cap_in = (float)(2.0 * 1.4426950408889634 * (double)a.scale / (double)softcap);
         cg.cap_out = (float)((double)softcap / (double)a.scale);
     }
-    return launch_kernel(prefill_fwd_kernel<D, IS_BF16, CAUSAL, false, kModeDense, FEAT>,
-                         dim3((unsigned)n_items), dim3(kThreads), (hipStream_t)a.stream,
-                         "prefill_fwd_kernel(variant)", a.Q, a.K, a.V, a.O, a.LSE, a.B, a.Hq,
-                         a.Hkv, a.N, scale_log2, n_qtiles, (int)n_items, xcd_major, cg, nullptr,
-                         nullptr, nullptr, 0);
+    return launch_prefill_t<D, IS_BF16, CAUSAL, FEAT>(a, cg);
 }
 
 template <int D, bool IS_BF16>
