@@ -441,6 +441,8 @@ def main():
     wall = time.perf_counter() - t0
     t_pre = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps * 1e-3   # seconds
     t_dec = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps * 1e-3
+    med_pre = float(np.median([e[0].elapsed_time(e[1]) for e in events])) * 1e-3
+    med_dec = float(np.median([e[1].elapsed_time(e[2]) for e in events])) * 1e-3
     assert torch.isfinite(LSE).all() and torch.isfinite(Ld).all()
 
     fl = prefill_flops(pc)
@@ -464,19 +466,22 @@ def main():
                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                         "traffic": pre_traffic, "kernel": "prefill_fwd_kernel<64,bf16,causal>",
                         "algorithmic_bytes_per_launch": pb,
-                        "avg_launch_us": round(t_pre * 1e6, 2)}
+                        "avg_launch_us": round(t_pre * 1e6, 2),
+                        "median_launch_us": round(med_pre * 1e6, 2)}
         else:
             roof_pre = {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_PEAK_TFLOPS, 4),
                         "traffic": pre_traffic, "kernel": "prefill_fwd_kernel<64,bf16,causal>",
-                        "avg_launch_us": round(t_pre * 1e6, 2)}
+                        "avg_launch_us": round(t_pre * 1e6, 2),
+                        "median_launch_us": round(med_pre * 1e6, 2)}
     roof_dec = None
     if do_dec:
         roof_dec = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                     "traffic": dec_traffic,
                     "kernel": "decode_split_kernel<128,bf16> + decode_merge_kernel<128,bf16>",
-                    "algorithmic_bytes_per_launch": db, "avg_launch_us": round(t_dec * 1e6, 2)}
+                    "algorithmic_bytes_per_launch": db, "avg_launch_us": round(t_dec * 1e6, 2),
+                    "median_launch_us": round(med_dec * 1e6, 2)}
 
     extra = {}
     if not args.no_extra and args.only is None:

@@ -171,3 +171,31 @@ def test_prefill_and_paged_prefill_graph_replays_equal_eager():
         n = int(cu[-1])
         assert torch.equal(POg[:n], PO2[:n]) and torch.equal(PLg[:n], PL2[:n]), \
             f"paged prefill replay {i}"
+
+
+def test_cascade_with_balanced_split_equals_the_explicit_split_bitwise():
+    import exact_attention_08_amd as attn
+    from attn_inputs import cascade_case
+    say("balanced split in the cascade decode")
+    own = [0, 300, 4096, 17, 1000, 2048, 5, 64]
+    c = cascade_case(len(own), 32, 8, 128, 3000, own, 16, BF16, seeds=(131, 132, 133))
+    q = to_dev(c.q, BF16)
+    K, V = to_dev(c.k_pages, BF16), to_dev(c.v_pages, BF16)
+    kpre, vpre = to_dev(c.extra["k_prefix"], BF16), to_dev(c.extra["v_prefix"], BF16)
+    bt = torch.from_numpy(c.block_table).cuda()
+    ctx = torch.from_numpy(c.ctx_lens).cuda()
+    ws = torch.empty(attn.attn_decode_cascade_workspace_bytes(c.B, 32, 128, 16, c.max_pages, 0,
+                                                              3000),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for split in (0, balanced_split(own, 8)):
+        O = torch.empty_like(q)
+        L = torch.empty(c.B, 32, dtype=torch.float32, device="cuda")
+        attn.attn_decode_cascade(q, kpre, vpre, K, V, bt, ctx, O, L, split, ws, c.scale)
+        torch.cuda.synchronize()
+        outs.append((O, L))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    O_ref, L_ref = oracle.decode_cascade(c.q, c.extra["k_prefix"], c.extra["v_prefix"],
+                                         c.k_pages, c.v_pages, c.block_table, c.ctx_lens,
+                                         c.scale, BF16)
+    assert_parity(from_dev_f64(outs[0][0]), O_ref, outs[0][1].cpu().numpy(), L_ref, "cascade balanced")
