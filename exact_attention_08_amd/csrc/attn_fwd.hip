@@ -529,6 +529,11 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             if constexpr (WIN) {
                 if (need_next && kb + 1 < NKB) read_k(ka, ST, kb + 1);
             }
+            // One workgroup per item: a wave issues step 4 at raised priority, so the SIMD's
+            // other wave, in its statistics step, fills the gaps instead of competing for
+            // the issue slots of the MFMA/exp stream (about 2% at N = 32768).  The persistent
+            // grid sets a per-item priority instead.
+            if constexpr (!PERSIST) __builtin_amdgcn_s_setprio(1);
             // 4. next S^T, this block's weights and O^T update (a live block always needs
             // the next S^T; with a window, so does the block just before the first live one)
             if constexpr (WIN) {
@@ -559,6 +564,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                     }
                 }
             }
+            if constexpr (!PERSIST) __builtin_amdgcn_s_setprio(0);
         };
 
         dma_tile(0, 0);
