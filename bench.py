@@ -363,6 +363,9 @@ def main():
                     default=None,
                     help="(profiling) run only one half of the step, or only the shared-prefix "
                          "decode or the paged prefill figure")
+    ap.add_argument("--profile-prefill", default=None, metavar="CONFIG",
+                    help="(profiling) only run attn_fwd on the named prefill configuration "
+                         "--steps times and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -381,6 +384,17 @@ def main():
     torch.cuda.set_device(dev)
     log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
 
+    if args.profile_prefill:
+        from attn_inputs import config_case as _cc
+        c = _cc(args.profile_prefill)
+        Qp, Kp, Vp = (to_dev(x, c.dtype) for x in (c.q, c.k, c.v))
+        Op = torch.empty_like(Qp)
+        Lp = torch.empty(c.B, c.Hq, c.N, dtype=torch.float32, device=dev)
+        for _ in range(args.steps):
+            attn.attn_fwd(Qp, Kp, Vp, Op, Lp, c.causal, c.scale)
+        torch.cuda.synchronize()
+        print(json.dumps({"profiled": args.profile_prefill, "launches": args.steps}), flush=True)
+        return
     if args.only == "cascade":
         print(json.dumps({"cascade_decode": cascade_figure(attn, torch, dev, log)}), flush=True)
         return
