@@ -13,6 +13,11 @@ missing the import fails, and a non-zero status from the library raises AttnErro
                         split_tokens, workspace, scale=None, stream=None)
     attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq, split_tokens,
                                         prefix_len)
+    attn_prefill_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens, O, LSE,
+                       max_q_len, causal=True, scale=None, stream=None)
+    attn_fwd_variant(Q, K, V, O, LSE, causal, window=0, softcap=0.0, scale=None, stream=None)
+
+split_tokens = 0 asks the decode calls for a split length chosen on the device.
 """
 from __future__ import annotations
 
