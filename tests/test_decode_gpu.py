@@ -155,3 +155,25 @@ def test_decode_named_workload_full_size_sampled_heads():
     O0, L0 = run_decode(case, c["split_tokens"], q_bits=np.zeros_like(case.q))
     cnt = np.round(np.exp(L0.cpu().numpy().astype(np.float64)))
     assert np.array_equal(cnt, np.repeat(case.ctx_lens[:, None].astype(float), case.Hq, 1))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,dtype,split,seed", [
+    (300, 8, 2, 64, BF16, 64, 41),      # more than 64 sequences: the work list from LDS tables
+    (1500, 4, 1, 64, FP16, 32, 42),     # more than 1024: the work list from wave-wide scans
+])
+def test_decode_large_batches_use_the_general_work_list(B, Hq, Hkv, d, dtype, split, seed):
+    say(f"decode large batch B{B} Hq{Hq} Hkv{Hkv} d{d} split{split}")
+    ctx = np.random.default_rng(seed).integers(0, 200, B).astype(np.int32)
+    case = decode_case(B, Hq, Hkv, d, ctx, 16, dtype, seeds=(seed, seed + 1, seed + 2),
+                       max_pages=16)
+    O, LSE = run_decode(case, split)
+    O_ref, L_ref = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                       case.ctx_lens, case.scale, dtype)
+    live = case.ctx_lens > 0
+    assert np.all(np.isneginf(LSE.cpu().numpy()[~live]))
+    assert_parity(from_dev_f64(O)[live], O_ref[live], LSE.cpu().numpy()[live], L_ref[live],
+                  "decode large batch")
+    # zero queries: exp(LSE) counts each sequence's tokens exactly
+    O0, L0 = run_decode(case, split, q_bits=np.zeros_like(case.q))
+    cnt = np.round(np.exp(L0.cpu().numpy().astype(np.float64)))
+    assert np.array_equal(cnt[live], np.repeat(ctx[live, None].astype(float), Hq, 1))
