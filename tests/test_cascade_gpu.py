@@ -124,3 +124,18 @@ def test_cascade_named_workload_full_size_sampled_heads(name):
     idx = torch.from_numpy(pairs).cuda()
     assert_parity(from_dev_f64(O.view(-1, case.d)[idx]), O_ref, LSE.view(-1)[idx].cpu().numpy(),
                   L_ref, name)
+
+
+def test_cascade_many_requests_span_several_prefix_query_tiles():
+    # 200 requests x 4 heads = 800 prefix query rows: seven 128-row tiles per kv head
+    say("cascade 200 requests")
+    own = np.random.default_rng(81).integers(0, 300, 200)
+    case = cascade_case(200, 32, 8, 128, 1000, own, 16, BF16, seeds=(82, 83, 84), max_pages=19)
+    O, LSE = run_cascade(case, 0)
+    rng = np.random.default_rng(85)
+    pairs = np.array(sorted({r * 32 + h for r in rng.integers(0, 200, 40) for h in (0, 5, 31)}),
+                     np.int64)
+    O_ref, L_ref = oracle_cascade(case, pairs=pairs)
+    idx = torch.from_numpy(pairs).cuda()
+    assert_parity(from_dev_f64(O.view(-1, case.d)[idx]), O_ref, LSE.view(-1)[idx].cpu().numpy(),
+                  L_ref, "cascade 200")
