@@ -238,7 +238,21 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 c.h = 0;
                 return c;
             } else if constexpr (PAGED) {
-                return prefill_work_item((int)blockIdx.x, n_qtiles, Hkv, 1, xcd_major);
+                WorkItem pw = prefill_work_item((int)blockIdx.x, n_qtiles, Hkv, 1, xcd_major);
+                // Batches of at most 64 requests: position b of the launch order is the
+                // request with the b-th longest cache (ties by index), so the heaviest items
+                // start first.  Each wave ranks the requests with shuffles; all agree.
+                if (B <= 64) {
+                    const int key = lane < B ? pg_kv_lens[lane] : -1;
+                    int rank = 0;
+                    for (int j = 0; j < 64; ++j) {
+                        const int kj = __shfl(key, j, 64);
+                        rank += (j < B && (kj > key || (kj == key && j < lane))) ? 1 : 0;
+                    }
+                    const unsigned long long hit = __ballot(lane < B && rank == pw.b);
+                    pw.b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+                }
+                return pw;
             } else {
                 return prefill_work_item(slot * P + x, n_qtiles, Hkv, G, xcd_major);
             }
