@@ -41,8 +41,13 @@
 //   * exp2 / log2 run on v_exp_f32 / v_log_f32 with log2(e) folded into the score scale.
 //   * Work order: the query heads sharing one K/V head, and all their query tiles, run on
 //     one XCD (one L2), heaviest causal tile first.  Short sequences use a persistent grid
-//     (one workgroup per resident slot taking items in turn), long ones one workgroup per
-//     item.
+//     (one workgroup per resident slot taking items in turn, each item at a pseudo-random
+//     issue priority), long ones one workgroup per item (each block's MFMA/exp region at
+//     raised issue priority).
+//
+// The same kernel serves three layouts (MODE: dense; the shared-prefix chunks of a cascade
+// decode; paged / varlen prefill) and two variants of the dense layout (FEAT: sliding window,
+// soft-cap); each is described where its geometry is defined below.
 #include <type_traits>
 
 #include "attn_common.h"
