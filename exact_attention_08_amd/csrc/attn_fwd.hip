@@ -386,7 +386,9 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         }
 
         // The KV sweep runs as a software pipeline over 32-key blocks.  Iteration b:
-        //   1. read block b's V operands; read the next block's K operands (same tile);
+        //   1. read block b's V operands; read the next block's K operands (same tile)
+        //      (at d = 128 these reads are issued one step earlier, at the end of step 4 of
+        //      the previous block);
         //   2. statistics of block b's scores (mask, max, the rare rescale) -- branches here;
         //   3. at the last block of a tile: wait until this wave's loads of the next tile have
         //      landed in LDS, barrier, start the loads of the tile after it into the stage just
@@ -451,6 +453,26 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             for (int ks = 0; ks < NKS; ++ks)
                 ka[ks] = *reinterpret_cast<const u32x4*>(lds_b + k_off[ks] + st * STAGE_B + kb * 32 * RB);
         };
+        auto read_v = [&](u32x4 (&va)[2][NDB], int st, int kb) {
+    #pragma unroll
+            for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const char* vp = lds_b + v_off[db] + st * STAGE_B + (kb * 32 + 16 * h) * RB;
+                    const u32x2 lo = read_tr(vp);
+                    const u32x2 hi = read_tr(vp + 8 * RB);
+                    va[h][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+        };
+        // At d = 128 without a window the operands are read one block ahead: at the end of a
+        // block's matrix region, into the registers its MFMAs have just consumed, the V^T
+        // operands of the next block and (at a tile's last block, whose barrier has published
+        // the next tile) the K operands of the block after it, so the reads have the next
+        // block's statistics step to land (N = 8192: 2% faster, bitwise identical).  At
+        // d = 64 it was slower.
+        constexpr bool HOIST = !WIN && D == 128;
+        u32x4 va_c[2][NDB];
+        u32x4 ka_c[NKS];
         auto s_product = [&](const u32x4 (&ka)[NKS], f32x16 (&sacc)[kQB]) {
     #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) {
@@ -471,21 +493,17 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             // here (with a window, also in the block just before its first live one)
             const bool live = WIN ? (bi >= nb_first && bi < nb_live) : bi < nb_live;   // wave-uniform
             const bool need_next = WIN ? (bi + 1 >= nb_first && bi < nb_live) : live;
-            u32x4 va[2][NDB];
-            u32x4 ka[NKS];
+            u32x4 va_l[2][NDB];
+            u32x4 ka_l[NKS];
+            u32x4 (&va)[2][NDB] = HOIST ? va_c : va_l;
+            u32x4 (&ka)[NKS] = HOIST ? ka_c : ka_l;
             float m_use[kQB];
             if (live) {
                 // 1. operands
-    #pragma unroll
-                for (int h = 0; h < 2; ++h)
-    #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const char* vp = lds_b + v_off[db] + ST * STAGE_B + (kb * 32 + 16 * h) * RB;
-                        const u32x2 lo = read_tr(vp);
-                        const u32x2 hi = read_tr(vp + 8 * RB);
-                        va[h][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                    }
-                if (!WIN && kb + 1 < NKB) read_k(ka, ST, kb + 1);
+                if constexpr (!HOIST) {
+                    read_v(va, ST, kb);
+                    if (!WIN && kb + 1 < NKB) read_k(ka, ST, kb + 1);
+                }
                 // 2. statistics
                 if constexpr (CAP) {
                     // soft-cap: s -> (c / scale) tanh(s scale / c), tanh(y) = 1 - 2 / (1 + e^2y)
@@ -583,6 +601,17 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                     }
                 }
             }
+            if constexpr (HOIST) {
+                if (bi + 1 < nb_live) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (kb + 1 < NKB) {
+                        read_v(va, ST, kb + 1);
+                    } else {
+                        read_v(va, 1 - ST, 0);
+                        read_k(ka, 1 - ST, 1);
+                    }
+                }
+            }
             if constexpr (!PERSIST) __builtin_amdgcn_s_setprio(0);
         };
 
@@ -597,6 +626,10 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             u32x4 ka[NKS];
             read_k(ka, 0, 0);
             s_product(ka, s_a);
+            if constexpr (HOIST) {
+                read_v(va_c, 0, 0);
+                read_k(ka_c, 0, 1);
+            }
         }
         // two tiles per trip, so that each block's LDS stage is a compile-time constant
         using st0 = std::integral_constant<int, 0>;
