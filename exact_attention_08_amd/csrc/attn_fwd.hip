@@ -121,6 +121,15 @@ template <int D> __device__ __forceinline__ int v_swz(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
+// max(a, b, c) in one instruction.  For finite inputs the scores are finite or -inf, so the
+// NaN canonicalisation the compiler adds to fmaxf's inputs is not needed (two fewer vector
+// instructions per block).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Shared-prefix (cascade) mode [CS349D Lecture 4 notes, 4.4 and 5.3]: the query rows of a
 // kv head are the single decode queries of all requests (request r, head kvh * G + g is row
 // r * G + g), so the prefix keys are read once for all of them; an item sweeps one chunk of
@@ -375,11 +384,14 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
 
         // a6 state, per column block (fp32, per lane = per query row; l is this lane's half
         // of the keys)
-        float m_ref[kQB], l_run[kQB];
+        // m_thr = m_ref + slack and m_exp (m_ref, or 0 while it is -inf) change only with m_ref
+        float m_ref[kQB], l_run[kQB], m_thr[kQB], m_exp[kQB];
         f32x16 oacc[kQB][NDB];
     #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
             m_ref[qb] = -INFINITY;
+            m_thr[qb] = -INFINITY;
+            m_exp[qb] = 0.f;
             l_run[qb] = 0.f;
     #pragma unroll
             for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
@@ -535,12 +547,13 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                     // maximum decides whether the reference may stay.  Only when some lane's
                     // half exceeds it are the two halves combined (lanes l and l^32 hold the
                     // same row), so both halves always agree on m_ref.
-                    float mloc = fmaxf(fmaxf(sc[qb][0], sc[qb][1]), sc[qb][2]);
+                    float mloc = max3f(sc[qb][0], sc[qb][1], sc[qb][2]);
     #pragma unroll
-                    for (int v = 3; v < 16; ++v) mloc = fmaxf(mloc, sc[qb][v]);
-                    if (__ballot(mloc * scale_log2 > m_ref[qb] + kRescaleSlack)) {
+                    for (int v = 3; v < 15; v += 2) mloc = max3f(mloc, sc[qb][v], sc[qb][v + 1]);
+                    mloc = max3f(mloc, sc[qb][15], sc[qb][15]);
+                    if (__ballot(mloc * scale_log2 > m_thr[qb])) {
                         const float m_blk = fmaxf(mloc, xor_lanes(mloc, 32)) * scale_log2;
-                        const bool move = m_blk > m_ref[qb] + kRescaleSlack;
+                        const bool move = m_blk > m_thr[qb];
                         const float m_new = move ? m_blk : m_ref[qb];
                         // 0 on the first block; a row that has seen no key yet (paged, or
                         // left of a window; reference still -inf) keeps alpha = 1
@@ -550,8 +563,10 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     #pragma unroll
                         for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
                         m_ref[qb] = m_new;
+                        m_thr[qb] = m_new + kRescaleSlack;
+                        m_exp[qb] = (m_new == -INFINITY) ? 0.f : m_new;
                     }
-                    m_use[qb] = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
+                    m_use[qb] = m_exp[qb];
                 }
             }
             // 3. tile boundary
