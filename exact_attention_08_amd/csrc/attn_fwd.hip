@@ -599,9 +599,9 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
     #pragma unroll
                     for (int v = 0; v < 16; ++v)
                         p[v] = fast_exp2(__builtin_fmaf(sc[qb][v], scale_log2, -m_use[qb]));
-                    float lsum = 0.f;
+                    float lsum = p[0];   // the weights are >= +0, so 0 + p[0] == p[0]
     #pragma unroll
-                    for (int v = 0; v < 16; ++v) lsum += p[v];
+                    for (int v = 1; v < 16; ++v) lsum += p[v];
                     l_run[qb] += lsum;
                     // a7: O^T += V^T P^T over the block's two 16-key steps
     #pragma unroll
