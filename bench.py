@@ -20,7 +20,11 @@ prefill over a paged cache (attn_prefill_paged), the sliding-window + soft-cap p
 (attn_fwd_variant), and the read bandwidth a plain streaming
 kernel reaches (the practical HBM ceiling).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--cpu-seconds 10] [--no-extra]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--cpu-seconds 10] [--no-extra]
+
+The GPU takes tens of milliseconds of sustained launches to reach its steady clock (a fresh
+N = 8192 prefill runs ~15% slower over its first ~30 launches), so the defaults warm up for
+50 steps (~30 ms) and the figures outside the step warm up for 0.1 s before they are timed.
 """
 from __future__ import annotations
 
@@ -87,6 +91,18 @@ def paged_prefill_flops(c):
     return 4.0 * c.Hq * c.d * pairs
 
 
+def warm(fn, torch, seconds=0.1, min_calls=3):
+    """Untimed calls until `seconds` of sustained GPU work have passed (steady clock)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_calls or time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def paged_prefill_figure(attn, torch, dev, log, reps=10):
     """Chunked prefill over a paged cache (PAGED_PREFILL workload).  Returns a dict for the
     JSON line."""
@@ -104,8 +120,7 @@ def paged_prefill_figure(attn, torch, dev, log, reps=10):
     def call():
         attn.attn_prefill_paged(q, kp, vp, bt, cu, kvl, O, L, c.max_q_len, c.causal, c.scale)
 
-    for _ in range(3):
-        call()
+    warm(call, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -148,8 +163,7 @@ def variant_figure(attn, torch, dev, log, reps=10):
     def call():
         attn.attn_fwd_variant(Q, K, V, O, L, True, v["window"], v["softcap"], c.scale)
 
-    for _ in range(2):
-        call()
+    warm(call, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -237,8 +251,7 @@ def cascade_figure(attn, torch, dev, log):
                                                              split), dtype=torch.uint8, device=dev)
 
     def timed(fn, reps=20):
-        for _ in range(3):
-            fn()
+        warm(fn, torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -352,8 +365,8 @@ def cpu_baseline(pc, dc, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
@@ -505,8 +518,7 @@ def main():
             Qx, Kx, Vx = (to_dev(x, c.dtype) for x in (c.q, c.k, c.v))
             Ox = torch.empty_like(Qx)
             Lx = torch.empty(c.B, c.Hq, c.N, dtype=torch.float32, device=dev)
-            for _ in range(2):
-                attn.attn_fwd(Qx, Kx, Vx, Ox, Lx, c.causal, c.scale)
+            warm(lambda: attn.attn_fwd(Qx, Kx, Vx, Ox, Lx, c.causal, c.scale), torch)
             reps = 10 if c.N <= 8192 else 4
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
