@@ -39,8 +39,12 @@
  *   - Results are bitwise deterministic for fixed inputs, shapes and split size: all
  *     reductions run in a fixed order.  (The decode's work queue takes tickets with an
  *     atomic counter; that decides only which workgroup computes an item, not how.)
- *   - The library keeps no state between calls and may be called from several host
- *     threads on different streams.
+ *   - The library keeps no host state between calls.  Each attn_decode_paged and
+ *     attn_decode_cascade launch takes the next of 64 device-side work-queue slots in
+ *     rotation and leaves it reset when its last workgroup finishes.  At most 64 such
+ *     launches may therefore be in flight on one device at a time, over all streams.
+ *     Within that limit the calls may be made from several host threads on different
+ *     streams.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
 #define EXACT_ATTENTION_ATTN_H
