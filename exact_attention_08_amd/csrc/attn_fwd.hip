@@ -481,7 +481,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
         // operands of the next block and (at a tile's last block, whose barrier has published
         // the next tile) the K operands of the block after it, so the reads have the next
         // block's statistics step to land (N = 8192: 2% faster, bitwise identical).  At
-        // d = 64 it was slower.
+        // d = 64 it gained nothing.
         constexpr bool HOIST = !WIN && D == 128;
         u32x4 va_c[2][NDB];
         u32x4 ka_c[NKS];
