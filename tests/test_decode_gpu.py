@@ -177,3 +177,38 @@ def test_decode_large_batches_use_the_general_work_list(B, Hq, Hkv, d, dtype, sp
     O0, L0 = run_decode(case, split, q_bits=np.zeros_like(case.q))
     cnt = np.round(np.exp(L0.cpu().numpy().astype(np.float64)))
     assert np.array_equal(cnt[live], np.repeat(ctx[live, None].astype(float), Hq, 1))
+
+
+def test_decode_work_queue_slots_wrap_around():
+    """Each launch takes the next of 64 device-side work-queue slots and leaves it reset.
+    150 back-to-back launches on one stream (the balanced split, whose length also lives in
+    the slot, alternating with explicit splits) wrap the slots twice; every output must equal
+    the first bitwise."""
+    import exact_attention_08_amd as attn
+    say("decode: 150 launches over the 64 work-queue slots")
+    ctx = [1, 700, 4100, 33, 2048, 5000]
+    case = decode_case(len(ctx), 8, 2, 128, ctx, 16, BF16, seeds=(91, 92, 93))
+    K, V = to_dev(case.k_pages, case.dtype), to_dev(case.v_pages, case.dtype)
+    q = to_dev(case.q, case.dtype)
+    bt = torch.from_numpy(case.block_table).cuda()
+    cl = torch.from_numpy(case.ctx_lens).cuda()
+    splits = (0, 256, 1024)
+    ws = {s: torch.empty(attn.attn_decode_paged_workspace_bytes(
+        case.B, case.Hq, case.d, case.page_size, case.max_pages, s), dtype=torch.uint8,
+        device="cuda") for s in splits}
+    outs = {s: [] for s in splits}
+    for i in range(150):
+        s = splits[i % 3]
+        O = torch.empty_like(q)
+        L = torch.empty(case.B, case.Hq, dtype=torch.float32, device="cuda")
+        attn.attn_decode_paged(q, K, V, bt, cl, O, L, s, ws[s], case.scale)
+        outs[s].append((O, L))
+    torch.cuda.synchronize()
+    for s in splits:
+        O0, L0 = outs[s][0]
+        for O, L in outs[s][1:]:
+            assert torch.equal(O, O0) and torch.equal(L, L0), s
+    O_ref, L_ref = oracle.decode_paged(case.q, case.k_pages, case.v_pages, case.block_table,
+                                       case.ctx_lens, case.scale, case.dtype)
+    assert_parity(from_dev_f64(outs[0][0][0]), O_ref, outs[0][0][1].cpu().numpy(), L_ref,
+                  "decode after slot wrap")
