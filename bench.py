@@ -23,8 +23,9 @@ kernel reaches (the practical HBM ceiling).
     python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--cpu-seconds 10] [--no-extra]
 
 The GPU takes tens of milliseconds of sustained launches to reach its steady clock (a fresh
-N = 8192 prefill runs ~15% slower over its first ~30 launches), so the defaults warm up for
-50 steps (~30 ms) and the figures outside the step warm up for 0.1 s before they are timed.
+N = 8192 prefill runs ~15% slower over its first ~30 launches), so the step's warm-up runs
+the --warmup steps and continues until 0.3 s of launches have passed, and the figures
+outside the step warm up for 0.1 s before they are timed.
 """
 from __future__ import annotations
 
@@ -47,6 +48,7 @@ EXTRA = ["llama3_8b_prefill_n8192_causal", "llama3_8b_prefill_n32768_causal"]
 CASCADE = "cascade_gqa_decode_b64_prefix8192_own128_4096"
 PAGED_PREFILL = "chunked_prefill_b16_hist1024_16384_chunk256_2048"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+WARM_SECONDS = 0.3             # minimum warm-up of the step (steady clock), whatever --warmup
 
 
 def prefill_flops(c):
@@ -230,7 +232,7 @@ def cascade_figure(attn, torch, dev, log):
     ctx = torch.from_numpy(c.ctx_lens).to(dev)
     O = torch.empty_like(q)
     L = torch.empty(c.B, c.Hq, dtype=torch.float32, device=dev)
-    ws = torch.empty(attn.attn_decode_cascade_workspace_bytes(c.B, c.Hq, c.d, page, c.max_pages,
+    ws = torch.zeros(attn.attn_decode_cascade_workspace_bytes(c.B, c.Hq, c.d, page, c.max_pages,
                                                               split, P),
                      dtype=torch.uint8, device=dev)
     # the plain layout: prefix pages first in the pool, shared by every request's table
@@ -247,7 +249,7 @@ def cascade_figure(attn, torch, dev, log):
     ctx_all = ctx + P
     O2 = torch.empty_like(q)
     L2 = torch.empty_like(L)
-    ws2 = torch.empty(attn.attn_decode_paged_workspace_bytes(c.B, c.Hq, c.d, page, npre + c.max_pages,
+    ws2 = torch.zeros(attn.attn_decode_paged_workspace_bytes(c.B, c.Hq, c.d, page, npre + c.max_pages,
                                                              split), dtype=torch.uint8, device=dev)
 
     def timed(fn, reps=20):
@@ -429,7 +431,7 @@ def main():
     ctx = torch.from_numpy(dc.ctx_lens).to(dev)
     Od = torch.empty_like(q)
     Ld = torch.empty(dc.B, dc.Hq, dtype=torch.float32, device=dev)
-    ws = torch.empty(attn.attn_decode_paged_workspace_bytes(dc.B, dc.Hq, dc.d, dc.page_size,
+    ws = torch.zeros(attn.attn_decode_paged_workspace_bytes(dc.B, dc.Hq, dc.d, dc.page_size,
                                                             dc.max_pages, split),
                      dtype=torch.uint8, device=dev)
     # a plain copy of known size, for calibrating HBM counters when profiled
@@ -453,10 +455,19 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    log(f"bench: {args.warmup} warm-up steps")
-    for _ in range(args.warmup):
+    # W warm-up steps, continued until WARM_SECONDS of sustained launches have passed: the
+    # GPU reaches its steady clock only after tens of milliseconds of work, so a small W
+    # alone would time part of the clock ramp.
+    log(f"bench: {args.warmup} warm-up steps (at least {WARM_SECONDS} s)")
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < WARM_SECONDS:
         step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"bench: {args.steps} timed steps")
@@ -550,6 +561,8 @@ def main():
         "value": round(pre_tflops, 2) if pre_tflops is not None else None,
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_detail": {"steps_run": n_warm, "seconds": round(warm_s, 3),
+                          "rule": f"--warmup steps, continued to at least {WARM_SECONDS} s"},
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded i.i.d. N(0,1), bf16)",

@@ -3,7 +3,7 @@
 The binding only marshals arguments: it reads shapes, device pointers and the current HIP
 stream from torch tensors and calls the C ABI declared in include/attn.h.  Every step of
 the computation runs in the library's HIP kernels.  There is no fallback: if libattn.so is
-missing the import fails, and a non-zero status from the library raises AttnError.
+missing every call fails with ImportError, and a non-zero status from the library raises AttnError.
 
     attn_fwd(Q, K, V, O, LSE, causal, scale=None, stream=None)
     attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_tokens,
@@ -27,19 +27,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
-
-if not os.path.exists(LIB_PATH):
-    raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m exact_attention_08_amd.build` "
-        "(there is no non-HIP implementation to fall back to)")
-
-# One HIP runtime per process: torch brings its own libamdhip64 (same soname as ROCm's).
-# Loading torch first makes libattn.so's libamdhip64 dependency bind to that copy, so the
-# streams and device pointers torch hands over belong to the runtime that launches the
-# kernels.  Loading libattn.so first would pull in a second runtime.
-import torch  # noqa: E402,F401  (imported for its HIP runtime)
-
-_lib = ctypes.CDLL(LIB_PATH)
+_lib = None
 
 
 def _hip_runtimes_mapped():
@@ -50,27 +38,52 @@ def _hip_runtimes_mapped():
         return []
 
 
-if len(_hip_runtimes_mapped()) > 1:
-    raise ImportError("two HIP runtimes are loaded in this process "
-                      f"({_hip_runtimes_mapped()}); import torch before loading libattn.so")
-_P, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-_lib.attn_fwd.argtypes = [_P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _f, _i, _P]
-_lib.attn_fwd.restype = _i
-_lib.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i, _f,
-                                   _i, _P, _sz, _P]
-_lib.attn_decode_paged.restype = _i
-_lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
-_lib.attn_decode_paged_workspace_bytes.restype = _sz
-_lib.attn_decode_cascade.argtypes = [_P, _P, _P, _i, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i,
-                                     _i, _i, _f, _i, _P, _sz, _P]
-_lib.attn_decode_cascade.restype = _i
-_lib.attn_decode_cascade_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
-_lib.attn_decode_cascade_workspace_bytes.restype = _sz
-_lib.attn_fwd_variant.argtypes = [_P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i, _f, _f, _i, _P]
-_lib.attn_fwd_variant.restype = _i
-_lib.attn_prefill_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i,
-                                    _i, _f, _i, _P]
-_lib.attn_prefill_paged.restype = _i
+def _load():
+    """Load libattn.so on first use and declare its argument types.
+
+    The package itself imports without the library, so that the build module
+    (exact_attention_08_amd.build) works from a clean checkout; every compute call goes
+    through here and fails with ImportError when the library is not built (there is no
+    non-HIP implementation to fall back to)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m exact_attention_08_amd.build` "
+            "(there is no non-HIP implementation to fall back to)")
+    # One HIP runtime per process: torch brings its own libamdhip64 (same soname as ROCm's).
+    # Loading torch first makes libattn.so's libamdhip64 dependency bind to that copy, so the
+    # streams and device pointers torch hands over belong to the runtime that launches the
+    # kernels.  Loading libattn.so first would pull in a second runtime.
+    import torch  # noqa: F401  (imported for its HIP runtime)
+
+    lib_ = ctypes.CDLL(LIB_PATH)
+    if len(_hip_runtimes_mapped()) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process "
+                          f"({_hip_runtimes_mapped()}); import torch before loading libattn.so")
+    _P, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib_.attn_fwd.argtypes = [_P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _f, _i, _P]
+    lib_.attn_fwd.restype = _i
+    lib_.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i,
+                                       _f, _i, _P, _sz, _P]
+    lib_.attn_decode_paged.restype = _i
+    lib_.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+    lib_.attn_decode_paged_workspace_bytes.restype = _sz
+    lib_.attn_decode_cascade.argtypes = [_P, _P, _P, _i, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i,
+                                         _i, _i, _i, _f, _i, _P, _sz, _P]
+    lib_.attn_decode_cascade.restype = _i
+    lib_.attn_decode_cascade_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+    lib_.attn_decode_cascade_workspace_bytes.restype = _sz
+    lib_.attn_fwd_variant.argtypes = [_P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i, _f, _f,
+                                      _i, _P]
+    lib_.attn_fwd_variant.restype = _i
+    lib_.attn_prefill_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i,
+                                        _i, _i, _f, _i, _P]
+    lib_.attn_prefill_paged.restype = _i
+    _lib = lib_
+    return _lib
+
 
 ATTN_OK = 0
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
@@ -90,7 +103,7 @@ class AttnError(RuntimeError):
 
 def lib():
     """The raw ctypes handle (argument types set), for callers that pass pointers."""
-    return _lib
+    return _load()
 
 
 def _dtype_code(t):
@@ -132,7 +145,7 @@ def attn_fwd(Q, K, V, O, LSE, causal: bool, scale: float | None = None, stream=N
     _need(K.dtype == Q.dtype and V.dtype == Q.dtype and O.dtype == Q.dtype, "dtypes must match")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    code = _lib.attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), LSE.data_ptr(),
+    code = _load().attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), LSE.data_ptr(),
                          B, Hq, K.shape[1], N, d, int(bool(causal)), float(scale), dt,
                          _stream_ptr(Q, stream))
     _check("attn_fwd", code)
@@ -154,7 +167,7 @@ def attn_fwd_variant(Q, K, V, O, LSE, causal: bool, window: int = 0, softcap: fl
     _need(K.dtype == Q.dtype and V.dtype == Q.dtype and O.dtype == Q.dtype, "dtypes must match")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    code = _lib.attn_fwd_variant(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+    code = _load().attn_fwd_variant(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
                                  LSE.data_ptr(), B, Hq, K.shape[1], N, d, int(bool(causal)),
                                  int(window), float(softcap), float(scale), dt,
                                  _stream_ptr(Q, stream))
@@ -163,7 +176,7 @@ def attn_fwd_variant(Q, K, V, O, LSE, causal: bool, window: int = 0, softcap: fl
 
 def attn_decode_paged_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq,
                                       split_tokens) -> int:
-    return int(_lib.attn_decode_paged_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq,
+    return int(_load().attn_decode_paged_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq,
                                                       split_tokens))
 
 
@@ -171,7 +184,8 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_
                       workspace, scale: float | None = None, stream=None) -> None:
     """O (and LSE unless None) <- paged split-KV decode.  q,O [B,Hq,d]; pages
     [num_pages,page,Hkv,d]; block_table int32 [B,max_pages]; ctx_lens int32 [B];
-    workspace: a device buffer of at least attn_decode_paged_workspace_bytes(...) bytes."""
+    workspace: a device buffer of at least attn_decode_paged_workspace_bytes(...) bytes,
+    zero-filled once after allocation (torch.zeros) and used by one call at a time."""
     import torch
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
                     ("block_table", block_table), ("ctx_lens", ctx_lens), ("O", O),
@@ -194,7 +208,7 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     ws_bytes = workspace.numel() * workspace.element_size()
-    code = _lib.attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+    code = _load().attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                   block_table.data_ptr(), ctx_lens.data_ptr(), O.data_ptr(),
                                   None if LSE is None else LSE.data_ptr(), B, Hq, Hkv, d, page,
                                   block_table.shape[1], int(split_tokens), float(scale), dt,
@@ -204,7 +218,7 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_
 
 def attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq, split_tokens,
                                         prefix_len) -> int:
-    return int(_lib.attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq,
+    return int(_load().attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq,
                                                         split_tokens, prefix_len))
 
 
@@ -238,7 +252,7 @@ def attn_decode_cascade(q, k_prefix, v_prefix, k_pages, v_pages, block_table, ct
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     ws_bytes = workspace.numel() * workspace.element_size()
-    code = _lib.attn_decode_cascade(q.data_ptr(), k_prefix.data_ptr() if P else None,
+    code = _load().attn_decode_cascade(q.data_ptr(), k_prefix.data_ptr() if P else None,
                                     v_prefix.data_ptr() if P else None, P, k_pages.data_ptr(),
                                     v_pages.data_ptr(), block_table.data_ptr(),
                                     ctx_lens.data_ptr(), O.data_ptr(),
@@ -278,7 +292,7 @@ def attn_prefill_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, kv_lens, 
     _need(all(t.dtype == q.dtype for t in (k_pages, v_pages, O)), "dtypes must match")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    code = _lib.attn_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+    code = _load().attn_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                    block_table.data_ptr(), cu_seqlens_q.data_ptr(),
                                    kv_lens.data_ptr(), O.data_ptr(),
                                    None if LSE is None else LSE.data_ptr(), B, Hq, Hkv, d, page,

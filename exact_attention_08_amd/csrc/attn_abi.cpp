@@ -87,11 +87,13 @@ extern "C" size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int pa
     return attn::decode_workspace_bytes(B, Hq, d, S);
 }
 
-extern "C" int attn_decode_paged(const void* q, const void* Kpages, const void* Vpages,
-                                 const int* block_table, const int* ctx_lens, void* O, float* LSE,
-                                 int B, int Hq, int Hkv, int d, int page_size,
-                                 int max_pages_per_seq, int split_tokens, float scale, int dtype,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+// Checks of a paged decode call (everything but the workspace).  On success *S_out is the
+// number of partial states per (sequence, head).
+int attn::check_decode_args(const void* q, const void* Kpages, const void* Vpages,
+                            const int* block_table, const int* ctx_lens, const void* O,
+                            const float* LSE, int B, int Hq, int Hkv, int d, int page_size,
+                            int max_pages_per_seq, int split_tokens, float scale, int dtype,
+                            long long* S_out) {
     if (!q || !Kpages || !Vpages || !block_table || !ctx_lens || !O) return ATTN_ERR_NULL;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
         split_tokens < 0 || Hq % Hkv != 0)
@@ -109,6 +111,20 @@ extern "C" int attn_decode_paged(const void* q, const void* Kpages, const void* 
     if (!aligned(q, 16) || !aligned(Kpages, 16) || !aligned(Vpages, 16) || !aligned(O, 16) ||
         !aligned(block_table, 4) || !aligned(ctx_lens, 4) || (LSE && !aligned(LSE, 4)))
         return ATTN_ERR_ALIGN;
+    *S_out = S;
+    return ATTN_OK;
+}
+
+extern "C" int attn_decode_paged(const void* q, const void* Kpages, const void* Vpages,
+                                 const int* block_table, const int* ctx_lens, void* O, float* LSE,
+                                 int B, int Hq, int Hkv, int d, int page_size,
+                                 int max_pages_per_seq, int split_tokens, float scale, int dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    long long S = 0;
+    const int st = attn::check_decode_args(q, Kpages, Vpages, block_table, ctx_lens, O, LSE, B,
+                                           Hq, Hkv, d, page_size, max_pages_per_seq,
+                                           split_tokens, scale, dtype, &S);
+    if (st != ATTN_OK) return st;
     if (!workspace) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
     if (workspace_bytes < attn::decode_workspace_bytes(B, Hq, d, S)) return ATTN_ERR_WORKSPACE;

@@ -39,7 +39,6 @@
 //     waves) halves the time per item, so the queue's last items end closer together, and
 //     no two workgroups on a CU compete.
 #include <algorithm>
-#include <atomic>
 
 #include "attn_common.h"
 #include "attn_internal.h"
@@ -54,15 +53,15 @@ constexpr int kDecThreads = 64 * kDecWaves;
 // A wave's pages per item up to which the page sweep is unrolled (1024-token splits)
 constexpr int kSweepUnroll = 8;
 
-// Work queues of the split kernel: per launch slot, [0] the next ticket, [1] the number of
-// workgroups that have finished and [2] the split length the launch used (read by the merge
-// kernel when the length was chosen on the device).  The last workgroup of a launch to finish puts the slot
-// back to zero, so it is ready for a later launch without any host-side reset.
-constexpr int kDecSchedSlots = 64;
+// The split kernel's work queue lives in the caller's workspace, in the control block at its
+// start: [0] the next ticket, [1] the number of workgroups that have finished,
+// [2] the split length the call used (read by the merge kernel when the length was chosen
+// on the device).  Words 0 and 1 start at zero (the workspace is zero-filled once by its
+// owner) and the last workgroup of a call to finish puts them back to zero, so the next call
+// on the same workspace needs no reset.  Calls on different workspaces share nothing.
 // Batches up to this size keep their per-sequence split counts in LDS (built once per
 // workgroup), so finding an item's sequence needs no global loads.
 constexpr int kSeqCache = 1024;
-__device__ unsigned g_decode_sched[kDecSchedSlots][4];
 
 template <int D, bool IS_BF16>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
@@ -70,7 +69,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     const uint16_t* __restrict__ Vp, const int* __restrict__ block_table,
     const int* __restrict__ ctx_lens, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int B, int Hq, int Hkv, int max_pages, int split_tokens, int S_max, float scale_log2,
-    int sched_slot, int n_workers) {
+    unsigned* __restrict__ queue, int n_workers) {
     using E = Elem<IS_BF16>;
     constexpr int NKS = D / 32;          // k-steps of S^T = K Q^T (32 dims each)
     constexpr int NDB = D / 16;          // 16-row d blocks of O^T
@@ -143,7 +142,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
             const int len = per <= 128 ? 256 : per <= 3072 ? 512 : per <= 10240 ? 1024 : 2048;
             if (lane == 0) {
                 s_split = len;
-                if (blockIdx.x == 0) g_decode_sched[sched_slot][2] = (unsigned)len;
+                if (blockIdx.x == 0) queue[2] = (unsigned)len;
             }
         }
         __syncthreads();
@@ -193,7 +192,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     };
     const int n_full = total_of(n_full_of);
     const int n_items = (n_full + total_of(n_part_of)) * Hkv;
-    unsigned* const queue = g_decode_sched[sched_slot];
 
     const bool cached = B <= kSeqCache;
     if (cached) {
@@ -228,9 +226,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
         __syncthreads();
     }
     // the sequence holding unit t of the cached prefix array pf (the first r with pf[r] > t)
+    // Lane-dependent addresses in the two helpers below are rederived at each use (the empty
+    // asm hides that the lane index is loop invariant): hoisted out of the item loop, they
+    // would stay live across the page sweep and push its registers into scratch.
+    auto fresh_tid = [] {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
     auto find_cached = [&](const int* pf, int t) {
+        const int ln = fresh_tid() & 63;
         for (int c0 = 0;; c0 += 64) {
-            const int v = c0 + lane < B ? pf[c0 + lane] : 0x7fffffff;
+            const int v = c0 + ln < B ? pf[c0 + ln] : 0x7fffffff;
             const unsigned long long hit = __ballot(v > t);
             if (hit) return __builtin_amdgcn_readfirstlane(c0 + __builtin_ctzll(hit));
         }
@@ -249,8 +256,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
         const int fv = it.valid ? ff : 0;
         const int t_item = fv / Hkv;
         it.kvh = fv % Hkv;
+        // an item past the list (which may be empty) is sequence 0, split 0, no tokens: no
+        // table is consulted, and its loads stay inside q (B >= 1) or read nothing
         int r = 0, split = 0, ctx = 0;
-        if (cached) {
+        if (it.valid && cached) {
             if (t_item < n_full) {
                 r = find_cached(s_pref[0], t_item);
                 split = t_item - (r > 0 ? s_pref[0][r - 1] : 0);
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
                 split = s_pref[0][r] - (r > 0 ? s_pref[0][r - 1] : 0);   // its full splits
                 ctx = s_ctx[r];
             }
-        } else {
+        } else if (it.valid) {
             if (t_item < n_full) {
                 locate(n_full_of, t_item, r, split);
             } else {
@@ -462,7 +471,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
         __syncthreads();
 
         const int64_t part = ((int64_t)it.r * Hq + it.kvh * G) * S_max;   // (r, first head) partials
-        for (int e = tid; e < G * D; e += kDecThreads) {
+        for (int e = fresh_tid(); e < G * D; e += kDecThreads) {
             const int hh = e / D, d = e % D;
             float m = -INFINITY;
 #pragma unroll
@@ -482,7 +491,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
         f = f_next;
         it = nx;
     }
-    // the last workgroup to finish resets the queue slot for a later launch
+    // the last workgroup to finish puts the counters back to zero for the next call on this
+    // workspace
     if (tid == 0) {
         __threadfence();
         if (atomicAdd(&queue[1], 1u) == gridDim.x - 1) {
@@ -503,7 +513,8 @@ template <int D, bool IS_BF16>
 __global__ __launch_bounds__(D) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const int* __restrict__ ctx_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int Hq, int split_tokens, int S_max, int n_pre, int s_base, int sched_slot) {
+    int Hq, int split_tokens, int S_max, int n_pre, int s_base,
+    const unsigned* __restrict__ queue) {
     using E = Elem<IS_BF16>;
     constexpr int NW = D / 64;                 // waves per workgroup
     __shared__ float s_w[D];
@@ -512,8 +523,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
     const int r = rh / Hq;
     const int d = threadIdx.x;
     const int ctx = ctx_lens[r];
-    // a split length chosen on the device was left in the launch's queue slot
-    if (split_tokens == 0) split_tokens = (int)g_decode_sched[sched_slot][2];
+    // a split length chosen on the device was left in the call's control block
+    if (split_tokens == 0) split_tokens = (int)queue[2];
     const int n_state = n_pre + (ctx + split_tokens - 1) / split_tokens;
     const float* lse_s = ws_lse + (int64_t)rh * S_max;
     const float* o_s = ws_o + (int64_t)rh * S_max * D;
@@ -568,8 +579,9 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     const long long S_split = decode_max_splits(a.page_size, a.max_pages, a.split_tokens);   // 0: shortest balanced split
     const long long n_pre = a.prefix_len > 0 ? cascade_chunks(a.prefix_len) : 0;
     const long long S = S_split + n_pre;
-    float* ws_o = (float*)a.workspace;
-    float* ws_lse = (float*)((char*)a.workspace + (size_t)a.B * a.Hq * (size_t)S * D * sizeof(float));
+    unsigned* queue = (unsigned*)a.workspace;
+    float* ws_o = (float*)((char*)a.workspace + kDecodeCtrlBytes);
+    float* ws_lse = (float*)((char*)ws_o + (size_t)a.B * a.Hq * (size_t)S * D * sizeof(float));
     if (n_pre > 0) {
         const CascadePrefixArgs pa{a.q, a.Kprefix, a.Vprefix, ws_o, ws_lse, a.B, a.Hq, a.Hkv, D,
                                    a.prefix_len, kCascadeChunk, (int)n_pre, (int)S, (int)S_split,
@@ -581,20 +593,15 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     const long long max_items = (long long)a.B * S_split * a.Hkv;
     const long long grid = std::min<long long>(max_items, (long long)device_cu_count());
-    // each launch takes the next queue slot; concurrent launches (different streams) use
-    // different slots as long as fewer than kDecSchedSlots are in flight on one device
-    static std::atomic<unsigned> launch_seq{0};
-    const int sched_slot =
-        (int)(launch_seq.fetch_add(1, std::memory_order_relaxed) % kDecSchedSlots);
     hipError_t e = launch_kernel(decode_split_kernel<D, IS_BF16>, dim3((unsigned)grid),
                                  dim3(kDecThreads), st, "decode_split_kernel", a.q, a.Kpages,
                                  a.Vpages, a.block_table, a.ctx_lens, ws_o, ws_lse, a.B, a.Hq,
                                  a.Hkv, a.max_pages, a.split_tokens, (int)S, scale_log2,
-                                 sched_slot, device_cu_count());
+                                 queue, device_cu_count());
     if (e != hipSuccess) return e;
     return launch_kernel(decode_merge_kernel<D, IS_BF16>, dim3((unsigned)(a.B * a.Hq)), dim3(D),
                          st, "decode_merge_kernel", ws_o, ws_lse, a.ctx_lens, a.O, a.LSE, a.Hq,
-                         a.split_tokens, (int)S, (int)n_pre, (int)S_split, sched_slot);
+                         a.split_tokens, (int)S, (int)n_pre, (int)S_split, queue);
 }
 
 }  // namespace

@@ -728,11 +728,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const ModeGeo& cg = ModeGeo{})
     // Short sequences: a persistent grid, one workgroup per resident slot (OCC per CU), so
     // CUs do not idle between short workgroups.  Long ones: one workgroup per item; there the
     // dispatcher's dynamic hand-out evens out the workgroups' different speeds.
-#ifdef PREFILL_PERSISTENT
-    const bool persistent = PREFILL_PERSISTENT;
-#else
     const bool persistent = a.N <= 2048;
-#endif
     const long long slots = (long long)device_cu_count() * PrefillTile<D>::OCC;
     const long long grid = persistent && n_items > slots ? slots : n_items;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);

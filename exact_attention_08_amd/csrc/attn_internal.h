@@ -96,6 +96,14 @@ hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStrea
 // Compute units of the current device (queried once per device, then cached).
 int device_cu_count();
 
+// Host-side checks of a paged decode call (all arguments but the workspace); returns an
+// attn_status and, on success, the partial states per (sequence, head) in *S_out.
+int check_decode_args(const void* q, const void* Kpages, const void* Vpages,
+                      const int* block_table, const int* ctx_lens, const void* O,
+                      const float* LSE, int B, int Hq, int Hkv, int d, int page_size,
+                      int max_pages_per_seq, int split_tokens, float scale, int dtype,
+                      long long* S_out);
+
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_cascade_prefix(const CascadePrefixArgs& a);
@@ -120,11 +128,14 @@ inline long long decode_max_splits(int page_size, int max_pages, int split_token
     return (max_tokens + len - 1) / len;
 }
 
-// Workspace layout: O partials [B][Hq][S][d] fp32, then LSE partials [B][Hq][S] fp32.
+// Workspace layout: the call's control block (work-queue counters, 256 bytes) first, at a
+// fixed place whatever the split, then O partials [B][Hq][S][d] fp32, then LSE partials
+// [B][Hq][S] fp32 (padded to 256 bytes).
+constexpr size_t kDecodeCtrlBytes = 256;
 inline size_t decode_workspace_bytes(int B, int Hq, int d, long long S) {
     const size_t o = (size_t)B * Hq * (size_t)S * d * sizeof(float);
     const size_t l = (size_t)B * Hq * (size_t)S * sizeof(float);
-    return o + ((l + 255) / 256) * 256;
+    return kDecodeCtrlBytes + o + ((l + 255) / 256) * 256;
 }
 
 }  // namespace attn

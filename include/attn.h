@@ -39,12 +39,12 @@
  *   - Results are bitwise deterministic for fixed inputs, shapes and split size: all
  *     reductions run in a fixed order.  (The decode's work queue takes tickets with an
  *     atomic counter; that decides only which workgroup computes an item, not how.)
- *   - The library keeps no host state between calls.  Each attn_decode_paged and
- *     attn_decode_cascade launch takes the next of 64 device-side work-queue slots in
- *     rotation and leaves it reset when its last workgroup finishes.  At most 64 such
- *     launches may therefore be in flight on one device at a time, over all streams.
- *     Within that limit the calls may be made from several host threads on different
- *     streams.
+ *   - The library is stateless: it keeps no host state and no device state between calls.
+ *     Everything a decode call needs beyond its inputs and outputs (partial states and the
+ *     work-queue counters of its persistent grid) lives in the caller's workspace, so a call
+ *     captured in a HIP graph touches only the buffers it was captured with.  Calls may be
+ *     made from several host threads on different streams; calls that are in flight at the
+ *     same time must not share a workspace.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
 #define EXACT_ATTENTION_ATTN_H
@@ -163,7 +163,12 @@ int attn_prefill_paged(const void* q, const void* Kpages, const void* Vpages,
  *   O            [B, Hq, d]                         dtype          (written)
  *   LSE          [B, Hq] float32, or NULL            (written when not NULL)
  *   workspace    >= attn_decode_paged_workspace_bytes(...) bytes, 16-byte aligned,
- *                device memory the library may overwrite (per-split partial states)
+ *                device memory owned by the caller: a 256-byte control block holding the
+ *                call's work-queue counters, then the per-split partial states.  The control
+ *                block (the first 256 bytes) must be zero before the first call that uses
+ *                the workspace (zero-fill it once after allocating it: hipMemset, or a fill
+ *                kernel); every call leaves it ready for the next call, whatever its split,
+ *                so later calls need no reset.  A workspace serves one call at a time.
  *
  *   Token t of sequence r is slot t % page_size of physical page block_table[r][t /
  *   page_size]; kv head kvh = h / (Hq / Hkv).  All ctx_lens[r] tokens are visible.  The
@@ -200,7 +205,8 @@ int attn_decode_paged(const void* q, const void* Kpages, const void* Vpages,
 /*
  * attn_decode_paged_workspace_bytes -- host-only helper: the workspace attn_decode_paged
  * needs for these sizes (partial outputs and LSEs of every split of every (sequence,
- * head)).  Returns 0 when the sizes are invalid.  Makes no HIP call.
+ * head), after the 256-byte control block).  Returns 0 when the sizes are invalid.  Makes
+ * no HIP call.
  */
 size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int page_size,
                                          int max_pages_per_seq, int split_tokens);
@@ -222,7 +228,8 @@ size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int page_size,
  *   Kpages, Vpages, block_table, ctx_lens, O, LSE, sizes, split_tokens, scale, dtype,
  *   workspace, stream: as in attn_decode_paged (ctx_lens counts only a request's own
  *   tokens).  A request with no keys at all gets O = 0 and LSE = -inf.
- *   workspace  at least attn_decode_cascade_workspace_bytes(...) bytes
+ *   workspace  at least attn_decode_cascade_workspace_bytes(...) bytes; zero-filled once
+ *              after allocation, one call at a time, as in attn_decode_paged
  *
  *   Supported: as attn_decode_paged; also B * Hq * d * 2 and prefix_len * d * 2 must not
  *   exceed 2^30 (32-bit addressing of q and of one prefix head).  Returns ATTN_OK or a
@@ -236,8 +243,9 @@ int attn_decode_cascade(const void* q, const void* Kprefix, const void* Vprefix,
 
 /*
  * attn_decode_cascade_workspace_bytes -- host-only helper: the workspace attn_decode_cascade
- * needs (the partial states of every split and every prefix chunk of every (request, head)).
- * Returns 0 when the sizes are invalid.  Makes no HIP call.
+ * needs (the partial states of every split and every prefix chunk of every (request, head),
+ * after the 256-byte control block).  Returns 0 when the sizes are invalid.  Makes no HIP
+ * call.
  */
 size_t attn_decode_cascade_workspace_bytes(int B, int Hq, int d, int page_size,
                                            int max_pages_per_seq, int split_tokens,

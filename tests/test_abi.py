@@ -96,7 +96,8 @@ def test_workspace_helper():
     S = (2048 * 16 + 1023) // 1024
     o = 64 * 32 * S * 128 * 4
     l = 64 * 32 * S * 4
-    assert ws(64, 32, 128, 16, 2048, 1024) == o + ((l + 255) // 256) * 256
+    # the 256-byte control block, the partial states, then their LSEs padded to 256 bytes
+    assert ws(64, 32, 128, 16, 2048, 1024) == 256 + o + ((l + 255) // 256) * 256
     assert ws(0, 32, 128, 16, 2048, 1024) == 0
     assert ws(1, 1, 64, 16, 1, 16) >= 64 * 4 + 4
 
@@ -134,7 +135,7 @@ def test_cascade_workspace_helper_adds_the_prefix_chunks():
     S = (2048 * 16 + 1023) // 1024 + 9
     o = 64 * 32 * S * 128 * 4
     l = 64 * 32 * S * 4
-    assert cw(64, 32, 128, 16, 2048, 1024, 4097) == o + ((l + 255) // 256) * 256
+    assert cw(64, 32, 128, 16, 2048, 1024, 4097) == 256 + o + ((l + 255) // 256) * 256
     assert cw(64, 32, 128, 16, 2048, 1024, -1) == 0
 
 
@@ -193,3 +194,4 @@ def fvar(Q=A, K=A, V=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, N=100, d=128, causal=1, wi
 ])
 def test_attn_fwd_variant_rejects_bad_arguments(kw, code):
     assert fvar(**kw) == code
+

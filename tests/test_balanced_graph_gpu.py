@@ -46,7 +46,7 @@ class Decode:
         self.ctx = torch.from_numpy(case.ctx_lens).cuda()
         self.O = torch.empty_like(self.q)
         self.L = torch.empty(case.B, case.Hq, dtype=torch.float32, device="cuda")
-        self.ws = torch.empty(attn.attn_decode_paged_workspace_bytes(
+        self.ws = torch.zeros(attn.attn_decode_paged_workspace_bytes(
             case.B, case.Hq, case.d, 16, case.max_pages, 0), dtype=torch.uint8, device="cuda")
 
     def __call__(self, split, O=None, L=None):
@@ -120,6 +120,70 @@ def test_decode_graph_replays_follow_changing_lengths():
     assert seen == {256, 512, 1024}
 
 
+def test_decode_graphs_on_two_streams_with_eager_calls_between():
+    """The decode keeps no state outside the caller's workspace: two captured graphs (each
+    with its own workspace) replayed at the same time on two streams, while more than 64
+    eager calls run on a third workspace, all give the eager result bit for bit."""
+    import exact_attention_08_amd as attn
+    say("graph: two decode graphs on two streams, 80 eager calls in between")
+    ca = decode_case(12, 32, 8, 128, log_uniform_ctx(12, 512, 16384, seed=71), 16, BF16,
+                     seeds=(72, 73, 74))
+    cb = decode_case(5, 16, 4, 64, [3000, 17, 0, 900, 5000], 16, FP16, seeds=(75, 76, 77))
+    da, db = Decode(ca), Decode(cb)
+    # eager references, each on a workspace of its own
+    ref = {}
+    for key, d, split in (("a", da, 0), ("b", db, 512)):
+        ws = torch.zeros(attn.attn_decode_paged_workspace_bytes(
+            d.c.B, d.c.Hq, d.c.d, 16, d.c.max_pages, split), dtype=torch.uint8, device="cuda")
+        O, L = torch.empty_like(d.O), torch.empty_like(d.L)
+        attn.attn_decode_paged(d.q, d.K, d.V, d.bt, d.ctx, O, L, split, ws, d.c.scale)
+        ref[key] = (O, L, ws)
+    torch.cuda.synchronize()
+    graphs = {}
+    for key, d, split in (("a", da, 0), ("b", db, 512)):
+        if split:
+            d.ws = torch.zeros(attn.attn_decode_paged_workspace_bytes(
+                d.c.B, d.c.Hq, d.c.d, 16, d.c.max_pages, split), dtype=torch.uint8,
+                device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            d(split)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            d(split)
+        graphs[key] = g
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        da.O.zero_()
+        db.O.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            graphs["a"].replay()
+        with torch.cuda.stream(s2):
+            graphs["b"].replay()
+        eager = []
+        wa = ref["a"][2]
+        for i in range(80):
+            O, L = torch.empty_like(da.O), torch.empty_like(da.L)
+            attn.attn_decode_paged(da.q, da.K, da.V, da.bt, da.ctx, O, L, 0, wa, ca.scale)
+            eager.append((O, L))
+        torch.cuda.synchronize()
+        assert torch.equal(da.O, ref["a"][0]) and torch.equal(da.L, ref["a"][1]), f"graph a {rep}"
+        assert torch.equal(db.O, ref["b"][0]) and torch.equal(db.L, ref["b"][1]), f"graph b {rep}"
+        for i, (O, L) in enumerate(eager):
+            assert torch.equal(O, ref["a"][0]) and torch.equal(L, ref["a"][1]), f"eager {i}"
+    for key, c in (("a", ca), ("b", cb)):
+        O_ref, L_ref = oracle.decode_paged(c.q, c.k_pages, c.v_pages, c.block_table, c.ctx_lens,
+                                           c.scale, c.dtype)
+        live = c.ctx_lens > 0
+        assert_parity(from_dev_f64(ref[key][0])[live], O_ref[live],
+                      ref[key][1].cpu().numpy()[live], L_ref[live], f"graph {key}")
+
+
 def test_prefill_and_paged_prefill_graph_replays_equal_eager():
     import exact_attention_08_amd as attn
     say("graph: attn_fwd and attn_prefill_paged replays")
@@ -184,7 +248,7 @@ def test_cascade_with_balanced_split_equals_the_explicit_split_bitwise():
     kpre, vpre = to_dev(c.extra["k_prefix"], BF16), to_dev(c.extra["v_prefix"], BF16)
     bt = torch.from_numpy(c.block_table).cuda()
     ctx = torch.from_numpy(c.ctx_lens).cuda()
-    ws = torch.empty(attn.attn_decode_cascade_workspace_bytes(c.B, 32, 128, 16, c.max_pages, 0,
+    ws = torch.zeros(attn.attn_decode_cascade_workspace_bytes(c.B, 32, 128, 16, c.max_pages, 0,
                                                               3000),
                      dtype=torch.uint8, device="cuda")
     outs = []

@@ -5,7 +5,7 @@ The oracle computes the definition: each request attends to the prefix keys foll
 own paged tokens.  Covered: GQA and MHA, both dtypes and head sizes, prefixes shorter than
 one tile, ragged and several chunks long; requests with no own tokens; no prefix (equal to
 attn_decode_paged, bitwise); bitwise determinism; the full-size shared-prefix workload on
-sampled heads.
+every (request, head).  Outputs start as NaN / +inf, so any pair left unwritten fails.
 """
 import sys
 
@@ -34,12 +34,14 @@ def run_cascade(case, split, want_lse=True):
     Vp = to_dev(case.extra["v_prefix"], case.dtype)
     bt = torch.from_numpy(case.block_table).cuda()
     ctx = torch.from_numpy(case.ctx_lens).cuda()
-    O = torch.empty_like(q)
-    LSE = torch.empty(case.B, case.Hq, dtype=torch.float32, device="cuda") if want_lse else None
+    # outputs start as NaN / +inf: a (request, head) the merge never writes fails every check
+    O = torch.full_like(q, float("nan"))
+    LSE = (torch.full((case.B, case.Hq), float("inf"), dtype=torch.float32, device="cuda")
+           if want_lse else None)
     P = case.extra["k_prefix"].shape[1]
     nbytes = attn.attn_decode_cascade_workspace_bytes(case.B, case.Hq, case.d, case.page_size,
                                                       case.max_pages, split, P)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     attn.attn_decode_cascade(q, Kp, Vp, K, V, bt, ctx, O, LSE, split, ws, case.scale)
     torch.cuda.synchronize()
     return O, LSE
@@ -79,7 +81,7 @@ def test_cascade_without_prefix_is_paged_decode_bitwise_and_deterministic():
     ctx = torch.from_numpy(case.ctx_lens).cuda()
     O2 = torch.empty_like(q)
     L2 = torch.empty(case.B, case.Hq, dtype=torch.float32, device="cuda")
-    ws = torch.empty(attn.attn_decode_paged_workspace_bytes(case.B, case.Hq, case.d, 16,
+    ws = torch.zeros(attn.attn_decode_paged_workspace_bytes(case.B, case.Hq, case.d, 16,
                                                             case.max_pages, 256),
                      dtype=torch.uint8, device="cuda")
     attn.attn_decode_paged(q, K, V, bt, ctx, O2, L2, 256, ws, case.scale)
@@ -108,22 +110,13 @@ def test_cascade_prefix_only_and_zero_query_counts():
 
 
 @pytest.mark.parametrize("name", sorted(CASCADE_WORKLOADS))
-def test_cascade_named_workload_full_size_sampled_heads(name):
+def test_cascade_named_workload_full_size_every_pair(name):
     c = CASCADE_WORKLOADS[name]
-    say(f"cascade full size {name}")
+    say(f"cascade full size {name}: every (request, head)")
     case = cascade_workload(name)
     O, LSE = run_cascade(case, c["split_tokens"])
-    assert torch.isfinite(O.float()).all() and torch.isfinite(LSE).all()
-    rng = np.random.default_rng(79)
-    rs = sorted({0, case.B - 1, int(np.argmax(case.ctx_lens)), int(np.argmin(case.ctx_lens))} |
-                set(rng.integers(0, case.B, 6).tolist()))
-    pairs = np.array([r * case.Hq + h for r in rs
-                      for h in sorted({0, 3, 4, 31} | set(rng.integers(0, 32, 2).tolist()))],
-                     np.int64)
-    O_ref, L_ref = oracle_cascade(case, pairs=pairs)
-    idx = torch.from_numpy(pairs).cuda()
-    assert_parity(from_dev_f64(O.view(-1, case.d)[idx]), O_ref, LSE.view(-1)[idx].cpu().numpy(),
-                  L_ref, name)
+    O_ref, L_ref = oracle_cascade(case)
+    assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, name)
 
 
 def test_cascade_many_requests_span_several_prefix_query_tiles():
@@ -132,10 +125,5 @@ def test_cascade_many_requests_span_several_prefix_query_tiles():
     own = np.random.default_rng(81).integers(0, 300, 200)
     case = cascade_case(200, 32, 8, 128, 1000, own, 16, BF16, seeds=(82, 83, 84), max_pages=19)
     O, LSE = run_cascade(case, 0)
-    rng = np.random.default_rng(85)
-    pairs = np.array(sorted({r * 32 + h for r in rng.integers(0, 200, 40) for h in (0, 5, 31)}),
-                     np.int64)
-    O_ref, L_ref = oracle_cascade(case, pairs=pairs)
-    idx = torch.from_numpy(pairs).cuda()
-    assert_parity(from_dev_f64(O.view(-1, case.d)[idx]), O_ref, LSE.view(-1)[idx].cpu().numpy(),
-                  L_ref, "cascade 200")
+    O_ref, L_ref = oracle_cascade(case)
+    assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, "cascade 200")

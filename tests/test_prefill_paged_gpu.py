@@ -7,7 +7,8 @@ than its chunk (queries that see no key), chunks spanning several tiles with rag
 bit-exact paging and masking (identity against shuffled block table, NaN poison in every
 slot the cache does not use and in a guard page before the pool, zero queries counting
 their visible keys exactly); a whole prompt equal bit for bit to attn_fwd; padding rows
-left untouched; determinism; the full-size chunked-prefill workload on sampled rows.
+left untouched; determinism; the full-size chunked-prefill workload on four rows of every
+work item (request, kv head, 128-row tile), with every output row checked as written.
 """
 import sys
 
@@ -39,7 +40,8 @@ def run_paged(case, k_pages=None, v_pages=None, table=None, q=None, want_lse=Tru
     cu = torch.from_numpy(case.cu_seqlens_q).cuda()
     kvl = torch.from_numpy(case.kv_lens).cuda()
     if O is None:
-        O = torch.zeros_like(qd)
+        # NaN until written: a row that should be computed and is not fails every check
+        O = torch.full_like(qd, float("nan"))
     L = torch.full((case.total_q, case.Hq), 7.0, dtype=torch.float32, device="cuda") \
         if want_lse else None
     attn.attn_prefill_paged(qd, K, V, bt, cu, kvl, O, L, case.max_q_len, case.causal,
@@ -171,20 +173,37 @@ def test_padding_rows_untouched_lse_optional_and_deterministic():
     check(case, O[:233].reshape(-1, 128), L[:233].reshape(-1), O_ref, L_ref, "padded")
 
 
-@pytest.mark.parametrize("name", sorted(PAGED_PREFILL_WORKLOADS))
-def test_paged_prefill_named_workload_full_size_sampled_rows(name):
-    say(f"paged prefill full size {name}")
-    case = paged_prefill_workload(name)
-    O, L = run_paged(case)
-    assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
-    rng = np.random.default_rng(43)
-    toks = set()
+def item_rows(case, seed):
+    """Four rows of every work item (request, kv head, 128-row tile of its G query heads x
+    new tokens): the tile's first row, a random row in each of the second and third 32-row
+    waves and the tile's last row, clipped to the request's rows.  A row t of a tile is new
+    token t / G of the request and query head kvh * G + t % G; returned as flat indices
+    token * Hq + head of O [total_q, Hq]."""
+    rng = np.random.default_rng(seed)
+    G = case.Hq // case.Hkv
+    rows = []
     for r in range(case.B):
         a, b = int(case.cu_seqlens_q[r]), int(case.cu_seqlens_q[r + 1])
-        toks |= {a, b - 1, int(rng.integers(a, b))}
-    rows = np.array([t * case.Hq + h for t in sorted(toks)
-                     for h in sorted({0, 5, 31} | set(rng.integers(0, 32, 1).tolist()))],
-                    np.int64)
+        n_rows = (b - a) * G
+        for kvh in range(case.Hkv):
+            for t0 in range(0, n_rows, 128):
+                picks = {t0, t0 + 32 + int(rng.integers(0, 32)), t0 + 64 + int(rng.integers(0, 32)),
+                         t0 + 127}
+                for t in sorted(min(p, n_rows - 1) for p in picks):
+                    rows.append((a + t // G) * case.Hq + kvh * G + t % G)
+    return np.array(sorted(set(rows)), np.int64)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(PAGED_PREFILL_WORKLOADS))
+def test_paged_prefill_named_workload_full_size_every_item(name):
+    say(f"paged prefill full size {name}: rows of every work item")
+    case = paged_prefill_workload(name)
+    O, L = run_paged(case)
+    # every row of every request was written (O started as NaN, LSE as 7.0)
+    assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
+    rows = item_rows(case, 43)
+    say(f"  oracle over {len(rows)} rows")
     O_ref, L_ref = oracle_paged(case, rows=rows)
     idx = torch.from_numpy(rows).cuda()
     check(case, O.view(-1, case.d)[idx], L.view(-1)[idx], O_ref, L_ref, name)
