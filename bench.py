@@ -370,6 +370,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="minimum duration of the step warm-up (0: exactly --warmup steps, "
+                         "for counter collection)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the Llama-3-8B prefill, shared-prefix decode and paged prefill "
@@ -458,10 +461,10 @@ def main():
     # W warm-up steps, continued until WARM_SECONDS of sustained launches have passed: the
     # GPU reaches its steady clock only after tens of milliseconds of work, so a small W
     # alone would time part of the clock ramp.
-    log(f"bench: {args.warmup} warm-up steps (at least {WARM_SECONDS} s)")
+    log(f"bench: {args.warmup} warm-up steps (at least {args.warm_seconds} s)")
     t_w = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_w < WARM_SECONDS:
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warm_seconds:
         step()
         n_warm += 1
         if n_warm % 8 == 0:
@@ -562,7 +565,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "warmup_detail": {"steps_run": n_warm, "seconds": round(warm_s, 3),
-                          "rule": f"--warmup steps, continued to at least {WARM_SECONDS} s"},
+                          "rule": f"--warmup steps, continued to at least {args.warm_seconds} s"},
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded i.i.d. N(0,1), bf16)",

@@ -591,7 +591,82 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             if constexpr (WIN) {
                 if (!live && need_next) s_product(ka, sn);
             }
-            if (live) {
+            if constexpr (HOIST) {
+                if (live) {
+                    // d = 128: the next block's S^T k-steps (one dependent chain) and this
+                    // block's O^T d-blocks (independent of it) alternate, one MFMA per slot,
+                    // with two of this block's weights in the slot after each MFMA:
+                    //   S0 w01 | S1 w23 | S2 w45 | S3 w67 pack0 | O00 w89 | S4 | O01 w1011 |
+                    //   S5 | O02 w1213 | S6 | O03 w1415 pack1 | S7 | O10 | O11 | O12 | O13
+                    // so the matrix pipe always has an instruction it can take while the vector
+                    // work issues behind it (the compiler's own order put up to eight vector
+                    // instructions between dependent S^T steps and all O^T MFMAs at the end).
+                    // The scheduling fences keep this order; N = 32768 ran 1.0% faster,
+                    // N = 8192 0.7%, N = 2048 1.9% (interleaved trials).
+                    static_assert(kQB == 1 && NKS == 8 && NDB == 4, "the slot order is for d = 128");
+                    float p[16];
+                    auto wgt = [&](int v) {
+                        p[v] = fast_exp2(__builtin_fmaf(sc[0][v], scale_log2, -m_use[0]));
+                    };
+                    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+                    auto pack = [&](int h) {
+                        return u32x4{E::pack2(p[8 * h + 0], p[8 * h + 1]), E::pack2(p[8 * h + 2], p[8 * h + 3]),
+                                     E::pack2(p[8 * h + 4], p[8 * h + 5]), E::pack2(p[8 * h + 6], p[8 * h + 7])};
+                    };
+                    // (written out statement by statement: in a loop the optimiser sinks the
+                    // S^T steps, whose result is used only at the end, past the O^T ones)
+                    fence();
+                    f32x16 sacc = E::mfma32(ka[0], qreg[0][0], f32x16{});
+                    fence(); wgt(0); wgt(1); fence();
+                    sacc = E::mfma32(ka[1], qreg[0][1], sacc);
+                    fence(); wgt(2); wgt(3); fence();
+                    sacc = E::mfma32(ka[2], qreg[0][2], sacc);
+                    fence(); wgt(4); wgt(5); fence();
+                    sacc = E::mfma32(ka[3], qreg[0][3], sacc);
+                    fence(); wgt(6); wgt(7);
+                    const u32x4 pk0 = pack(0);
+                    fence();
+                    oacc[0][0] = E::mfma32(va[0][0], pk0, oacc[0][0]);
+                    fence(); wgt(8); wgt(9); fence();
+                    sacc = E::mfma32(ka[4], qreg[0][4], sacc);
+                    fence();
+                    // the row sum in the order of the other paths (p0 + p1 + ... + p15), so
+                    // that results are bitwise those of the window and soft-cap variants
+                    float lsum = p[0];
+                    lsum += p[1]; lsum += p[2]; lsum += p[3];
+                    fence();
+                    oacc[0][1] = E::mfma32(va[0][1], pk0, oacc[0][1]);
+                    fence(); wgt(10); wgt(11); fence();
+                    sacc = E::mfma32(ka[5], qreg[0][5], sacc);
+                    fence();
+                    lsum += p[4]; lsum += p[5]; lsum += p[6]; lsum += p[7];
+                    fence();
+                    oacc[0][2] = E::mfma32(va[0][2], pk0, oacc[0][2]);
+                    fence(); wgt(12); wgt(13); fence();
+                    sacc = E::mfma32(ka[6], qreg[0][6], sacc);
+                    fence();
+                    lsum += p[8]; lsum += p[9]; lsum += p[10]; lsum += p[11];
+                    fence();
+                    oacc[0][3] = E::mfma32(va[0][3], pk0, oacc[0][3]);
+                    fence(); wgt(14); wgt(15);
+                    const u32x4 pk1 = pack(1);
+                    fence();
+                    sacc = E::mfma32(ka[7], qreg[0][7], sacc);
+                    fence();
+                    lsum += p[12]; lsum += p[13]; lsum += p[14]; lsum += p[15];
+                    fence();
+                    oacc[0][0] = E::mfma32(va[1][0], pk1, oacc[0][0]);
+                    fence();
+                    oacc[0][1] = E::mfma32(va[1][1], pk1, oacc[0][1]);
+                    fence();
+                    oacc[0][2] = E::mfma32(va[1][2], pk1, oacc[0][2]);
+                    fence();
+                    oacc[0][3] = E::mfma32(va[1][3], pk1, oacc[0][3]);
+                    fence();
+                    l_run[0] += lsum;
+                    sn[0] = sacc;
+                }
+            } else if (live) {
                 s_product(ka, sn);
     #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
@@ -664,7 +739,8 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
             const int q = q0w + 32 * qb + l32;
             if (q >= n_qrows) continue;
             const float l_tot = l_run[qb] + xor_lanes(l_run[qb], 32);
-            const float inv_l = 1.f / l_tot;
+            // v_rcp_f32 (about 1 ulp of fp32): far below the 16-bit rounding of the output
+            const float inv_l = __builtin_amdgcn_rcpf(l_tot);
             if constexpr (CASC) {
                 // partial state of (request, head) for this chunk: O~/l in fp32, and LSE
                 const int rr = q / G;
@@ -688,7 +764,7 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 // (a cache shorter than its chunk) gets O = 0 and LSE = -inf
                 const int qi = q / G;
                 const int64_t row = (int64_t)(pq0 + qi) * Hq + wi.kvh * G + (q - qi * G);
-                const float inv_p = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                const float inv_p = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
                 uint16_t* prow = O + row * D;
     #pragma unroll
                 for (int db = 0; db < NDB; ++db)
