@@ -8,6 +8,8 @@ missing every call fails with ImportError, and a non-zero status from the librar
     attn_fwd(Q, K, V, O, LSE, causal, scale=None, stream=None)
     attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_tokens,
                       workspace, scale=None, stream=None)
+    attn_decode_paged_noalloc(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_tokens,
+                              scale=None, stream=None)
     attn_decode_paged_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq, split_tokens)
     attn_decode_cascade(q, k_prefix, v_prefix, k_pages, v_pages, block_table, ctx_lens, O, LSE,
                         split_tokens, workspace, scale=None, stream=None)
@@ -68,6 +70,9 @@ def _load():
     lib_.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i, _i, _i,
                                        _f, _i, _P, _sz, _P]
     lib_.attn_decode_paged.restype = _i
+    lib_.attn_decode_paged_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i, _i,
+                                               _i, _i, _f, _i, _P]
+    lib_.attn_decode_paged_noalloc.restype = _i
     lib_.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
     lib_.attn_decode_paged_workspace_bytes.restype = _sz
     lib_.attn_decode_cascade.argtypes = [_P, _P, _P, _i, _P, _P, _P, _P, _P, _P, _i, _i, _i, _i,
@@ -88,9 +93,10 @@ def _load():
 ATTN_OK = 0
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
           -4: "ATTN_ERR_UNSUPPORTED", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_WORKSPACE",
-          -7: "ATTN_ERR_HIP"}
+          -7: "ATTN_ERR_HIP", -8: "ATTN_ERR_TOO_LARGE"}
 ATTN_BF16, ATTN_FP16 = 0, 1
-EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
+EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_noalloc",
+           "attn_decode_paged_workspace_bytes",
            "attn_decode_cascade", "attn_decode_cascade_workspace_bytes", "attn_prefill_paged",
            "attn_fwd_variant")
 
@@ -214,6 +220,39 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, ctx_lens, O, LSE, split_
                                   block_table.shape[1], int(split_tokens), float(scale), dt,
                                   workspace.data_ptr(), ws_bytes, _stream_ptr(q, stream))
     _check("attn_decode_paged", code)
+
+
+def attn_decode_paged_noalloc(q, k_pages, v_pages, block_table, ctx_lens, O, LSE,
+                              split_tokens: int, scale: float | None = None, stream=None) -> None:
+    """attn_decode_paged without a workspace: the library's fixed per-GPU scratch holds the
+    partial states (for callers that cannot allocate).  Calls that overlap on one GPU race;
+    a call whose partial states exceed the scratch raises AttnError (ATTN_ERR_TOO_LARGE)."""
+    import torch
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("block_table", block_table), ("ctx_lens", ctx_lens), ("O", O)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(q.dim() == 3 and O.shape == q.shape, "q,O must be [B,Hq,d]")
+    B, Hq, d = q.shape
+    _need(k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "pages must be [P,page,Hkv,d]")
+    _, page, Hkv, d2 = k_pages.shape
+    _need(d2 == d, "page head dim must match q")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+          "block_table must be int32 [B,max_pages]")
+    _need(ctx_lens.dtype == torch.int32 and tuple(ctx_lens.shape) == (B,), "ctx_lens must be int32 [B]")
+    if LSE is not None:
+        _need(LSE.is_cuda and LSE.is_contiguous() and LSE.dtype == torch.float32 and
+              tuple(LSE.shape) == (B, Hq), "LSE must be fp32 [B,Hq]")
+    dt = _dtype_code(q)
+    _need(k_pages.dtype == q.dtype and v_pages.dtype == q.dtype and O.dtype == q.dtype,
+          "dtypes must match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _load().attn_decode_paged_noalloc(
+        q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+        ctx_lens.data_ptr(), O.data_ptr(), None if LSE is None else LSE.data_ptr(), B, Hq, Hkv,
+        d, page, block_table.shape[1], int(split_tokens), float(scale), dt,
+        _stream_ptr(q, stream))
+    _check("attn_decode_paged_noalloc", code)
 
 
 def attn_decode_cascade_workspace_bytes(B, Hq, d, page_size, max_pages_per_seq, split_tokens,

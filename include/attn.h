@@ -39,7 +39,8 @@
  *   - Results are bitwise deterministic for fixed inputs, shapes and split size: all
  *     reductions run in a fixed order.  (The decode's work queue takes tickets with an
  *     atomic counter; that decides only which workgroup computes an item, not how.)
- *   - The library is stateless: it keeps no host state and no device state between calls.
+ *   - The library is stateless (attn_decode_paged_noalloc excepted, by design: it keeps a
+ *     fixed device buffer per GPU): it keeps no host state and no device state between calls.
  *     Everything a decode call needs beyond its inputs and outputs (partial states and the
  *     work-queue counters of its persistent grid) lives in the caller's workspace, so a call
  *     captured in a HIP graph touches only the buffers it was captured with.  Calls may be
@@ -67,7 +68,9 @@ enum attn_status {
                                /* of page_size                                                 */
     ATTN_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned                      */
     ATTN_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the helper's size             */
-    ATTN_ERR_HIP = -7          /* the HIP runtime reported an error at launch                  */
+    ATTN_ERR_HIP = -7,         /* the HIP runtime reported an error at launch                  */
+    ATTN_ERR_TOO_LARGE = -8    /* attn_decode_paged_noalloc: the call needs more scratch than  */
+                               /* the library's fixed buffer holds                             */
 };
 
 /* Element type of Q, K, V, O (and q, K/V pages, O for decode). */
@@ -210,6 +213,35 @@ int attn_decode_paged(const void* q, const void* Kpages, const void* Vpages,
  */
 size_t attn_decode_paged_workspace_bytes(int B, int Hq, int d, int page_size,
                                          int max_pages_per_seq, int split_tokens);
+
+/*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace and allocates nothing (no hipMalloc, no allocating
+ * library routine): the partial states and the work-queue counters live in a fixed device
+ * buffer of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until
+ * the process ends.  Arguments, results and errors as attn_decode_paged; same kernels, so
+ * the output is bitwise equal to attn_decode_paged's for the same inputs and split.
+ *
+ *   Limit: the call's partial states, sized as attn_decode_paged_workspace_bytes(B, Hq, d,
+ *   page_size, max_pages_per_seq, split_tokens) reports, must fit the buffer; a larger call
+ *   is rejected with ATTN_ERR_TOO_LARGE before anything is launched.  (The 64-sequence,
+ *   32-head, d = 128 batch with up to 2048 pages per sequence fits with 1024-token splits,
+ *   not with the balanced split, which is sized for 256-token splits.)
+ *   The first call on a device looks up the buffer's address (hipGetSymbolAddress) and
+ *   enqueues a small kernel that clears its control block; every call leaves the block
+ *   ready for the next.  All calls on one GPU share the buffer: calls that overlap in time
+ *   on one GPU (different streams, or graphs replayed concurrently) race and give wrong
+ *   results.  Serialise them, or use attn_decode_paged with a workspace per stream.
+ *   The stream must belong to the device the data live on.  Returns ATTN_OK or a negative
+ *   attn_status.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_decode_paged_noalloc(const void* q, const void* Kpages, const void* Vpages,
+                              const int* block_table, const int* ctx_lens, void* O, float* LSE,
+                              int B, int Hq, int Hkv, int d, int page_size,
+                              int max_pages_per_seq, int split_tokens, float scale, int dtype,
+                              void* stream);
 
 /*
  * attn_decode_cascade -- shared-prefix (cascade) decode [CS349D Lecture 4 notes, 4.4 and

@@ -195,3 +195,31 @@ def fvar(Q=A, K=A, V=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, N=100, d=128, causal=1, wi
 def test_attn_fwd_variant_rejects_bad_arguments(kw, code):
     assert fvar(**kw) == code
 
+
+def noalloc(q=A, K=A, V=A, bt=A, ctx=A, O=A, LSE=A, B=2, Hq=8, Hkv=2, d=128, page=16,
+            max_pages=8, split=64, scale=0.1, dtype=0):
+    return L.attn_decode_paged_noalloc(q, K, V, bt, ctx, O, LSE, B, Hq, Hkv, d, page, max_pages,
+                                       split, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(ctx=None), -1), (dict(O=None), -1),
+    (dict(B=0), -2), (dict(Hq=7), -2), (dict(split=-16), -2), (dict(scale=0.0), -2),
+    (dict(dtype=5), -3),
+    (dict(d=80), -4), (dict(page=32), -4), (dict(split=24), -4),
+    (dict(q=MIS), -5), (dict(bt=A + 2), -5),
+    # partial states beyond the fixed scratch: rejected before any HIP call
+    (dict(B=64, Hq=32, max_pages=2048, split=0), -8),
+    (dict(B=1, Hq=16, max_pages=65536, split=16), -2),
+])
+def test_attn_decode_paged_noalloc_rejects_bad_arguments(kw, code):
+    assert noalloc(**kw) == code
+
+
+def test_noalloc_scratch_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    cap = int(m.group(1)) << int(m.group(2))
+    ws = L.attn_decode_paged_workspace_bytes
+    # the 64-sequence decode batch with 1024-token splits fits; with the balanced split not
+    assert ws(64, 32, 128, 16, 2048, 1024) <= cap < ws(64, 32, 128, 16, 2048, 0)
