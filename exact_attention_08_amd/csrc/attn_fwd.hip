@@ -93,6 +93,30 @@ __device__ inline WorkItem prefill_work_item(int bid, int n_qtiles, int Hkv, int
     return w;
 }
 
+// Persistent grid: the order in which one XCD's workgroups take its n_x items (items are
+// numbered head-major, heaviest causal tile first within a head group of `per` items).  The
+// workgroups take the items in rounds of W, alternating direction, so in head-major order
+// each pair of rounds gives every workgroup one heavy and one light tile of the same head
+// groups.  The last round is partial, though, and in head-major order its items are heavy
+// tiles for some workgroups and none for others.  So only the rounds before the last two
+// full ones (an even number of them, keeping their pairs whole) stay head-major, and the
+// head groups left for the tail are taken heaviest tile first across all of them: the
+// lightest tiles then make up the partial round.  slot -> head-major item index, a bijection.
+// (Modelled on the GPT-2-medium grid with each item costing its tiles plus ~3 tiles of fixed
+// cost: the slowest workgroup's load falls from 1.085 to 1.024 times the mean.)
+__device__ inline int persistent_order(int s, int n_x, int W, int per, int G) {
+    const int R = (n_x + W - 1) / W;
+    const int full = R - 1;
+    const int hm = full < 2 ? 0 : full - (((full - 2) & 1) ? 3 : 2);
+    const int S0 = (max(hm, 0) * W / per) * per;
+    if (s < S0) return s;
+    const int t = s - S0;
+    const int hg0 = S0 / per;
+    const int span = (n_x / per - hg0) * G;   // tail items of one tile rank
+    const int rank = t / span, rem = t - rank * span;
+    return (hg0 + rem / G) * per + rank * G + rem % G;
+}
+
 __device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
@@ -268,7 +292,8 @@ __global__ __launch_bounds__(kThreads, PrefillTile<D>::OCC) void prefill_fwd_ker
                 }
                 return pw;
             } else {
-                return prefill_work_item(slot * P + x, n_qtiles, Hkv, G, xcd_major);
+                const int idx = PERSIST ? persistent_order(slot, n_slots, W, n_qtiles * G, G) : slot;
+                return prefill_work_item(idx * P + x, n_qtiles, Hkv, G, xcd_major);
             }
         }();
         // paged mode: the request's packed query rows and cache length (clamped to what the

@@ -69,10 +69,15 @@ def test_prefill_small_all_elements(B, Hq, Hkv, N, d, causal, dtype):
 
 
 # Short sequences with more query tiles than resident workgroup slots (768 at d = 64, 512 at
-# d = 128) run on the persistent grid, where one workgroup takes several items in turn.
+# d = 128) run on the persistent grid, where one workgroup takes several items in turn, in
+# head-major rounds and then a tail ordered by tile weight.
 PERSISTENT = [
     (16, 16, 16, 400, 64, True, BF16),
     (8, 16, 4, 520, 128, True, FP16),
+    # head groups not a multiple of 8 (one item list for the whole grid): two rounds (the
+    # whole order sorted by tile weight), and five (head-major rounds, then the sorted tail)
+    (9, 12, 3, 900, 64, True, BF16),
+    (25, 16, 4, 1024, 64, True, BF16),
 ]
 
 
