@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libattn.so")
 # the benchmark's streaming-read kernel (HBM ceiling), a library of its own
 PROBE_SRC = "hbm_probe.hip"
 PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
-SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_noalloc.hip", "attn_abi.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_d128.hip", "attn_decode.hip", "attn_noalloc.hip", "attn_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -105,6 +105,10 @@ int check_decode_args(const void* q, const void* Kpages, const void* Vpages,
                       long long* S_out);
 
 hipError_t launch_prefill(const PrefillArgs& a);
+// head size 128, long sequences: the 64-rows-per-wave kernel (attn_fwd_d128.hip), whose
+// results equal those of the 32-rows-per-wave prefill kernel bit for bit
+bool prefill_d128_applies(const PrefillArgs& a);
+hipError_t launch_prefill_d128(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_cascade_prefix(const CascadePrefixArgs& a);
 hipError_t launch_prefill_paged(const PagedPrefillArgs& a);

@@ -5,7 +5,8 @@ writes fails every check.  Small shapes are compared element by element over eve
 they span several 128-row query tiles and 64/128-key KV tiles and end on ragged tails.  The
 named workloads run at their full sizes in the launch configuration the benchmark times:
 the single-head, GPT-2-medium and N = 8192 ones are compared with the oracle on every
-element; at N = 32768 (8.8 TFLOP of fp64 for the whole output) four rows of every (head,
+element (head size 128 beyond 2048 keys runs the 64-rows-per-wave kernel, which is also
+checked on every element at smaller sizes); at N = 32768 (8.8 TFLOP of fp64 for the whole output) four rows of every (head,
 128-row query tile) pair are, one in each wave's 32 rows and both tile edges among them.
 At full size the zero-query test also checks every row exactly: each score is 0, so
 exp(LSE) must round to the number of visible keys and O must be the mean of the visible V
@@ -88,6 +89,27 @@ def test_prefill_persistent_grid_all_elements(B, Hq, Hkv, N, d, causal, dtype):
     O, LSE = run_fwd(case)
     O_ref, L_ref = oracle.attention(case.q, case.k, case.v, causal, case.scale, dtype)
     assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, "prefill persistent")
+
+
+# Head size 128 with more than 2048 keys and at least two 256-row items per CU runs the
+# 64-rows-per-wave kernel: both dtypes, causal and not, grouped heads, N a multiple of
+# neither 64 nor 256 (ragged last KV tile and query tile), several items per head group.
+D128 = [
+    (1, 32, 8, 4096, 128, True, BF16),
+    (1, 48, 6, 3001, 128, True, FP16),
+    (2, 16, 2, 4160, 128, False, BF16),
+    (2, 16, 4, 4100, 128, True, FP16),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,dtype", D128)
+def test_prefill_d128_kernel_all_elements(B, Hq, Hkv, N, d, causal, dtype):
+    say(f"prefill d128 kernel B{B} Hq{Hq} Hkv{Hkv} N{N} causal{causal} dtype{dtype}")
+    case = prefill_case(B, Hq, Hkv, N, d, causal, dtype, seeds=(21, 22, 23))
+    O, LSE = run_fwd(case)
+    O_ref, L_ref = oracle.attention(case.q, case.k, case.v, causal, case.scale, dtype)
+    assert_parity(from_dev_f64(O), O_ref, LSE.cpu().numpy(), L_ref, "prefill d128")
 
 
 def test_prefill_repeated_and_concurrent_launches_agree_bitwise():

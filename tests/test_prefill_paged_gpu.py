@@ -138,11 +138,13 @@ def test_paged_prefill_zero_queries_count_visible_keys():
     assert np.array_equal(cnt, np.repeat(want[:, None].astype(float), 32, 1))
 
 
-@pytest.mark.parametrize("d,dtype", [(128, BF16), (64, FP16)])
-def test_whole_prompt_equals_attn_fwd_bitwise(d, dtype):
-    say(f"paged prefill of a whole prompt vs attn_fwd d{d}")
+# N = 4160 at d = 128: attn_fwd runs the 64-rows-per-wave kernel there, the paged mode the
+# 32-rows-per-wave one, so the two kernels must agree bit for bit
+@pytest.mark.parametrize("d,dtype,N", [(128, BF16, 1000), (64, FP16, 1000), (128, BF16, 4160),
+                                       (128, FP16, 4160)])
+def test_whole_prompt_equals_attn_fwd_bitwise(d, dtype, N):
+    say(f"paged prefill of a whole prompt vs attn_fwd d{d} N{N}")
     import exact_attention_08_amd as attn
-    N = 1000
     case = paged_prefill_case(32, 8, d, [N], [N], 16, dtype, True, seeds=(37, 38, 39))
     O, L = run_paged(case)
     toks = np.arange(N)
