@@ -494,7 +494,7 @@ def main():
     # the prefill's algorithmic intensity is below the ridge (8 TB/s x time > 2.5 PF x time),
     # so its roofline is the HBM one
     pre_bound_hbm = pb / (HBM_PEAK_GBS * 1e9) > fl / (MFMA_PEAK_TFLOPS * 1e12)
-    pre_digest = source_digest(["attn_fwd.hip", "attn_common.h"])
+    pre_digest = source_digest(["attn_fwd.hip", "attn_common.h", "attn_prefill_common.h"])
     dec_digest = source_digest(["attn_decode.hip", "attn_common.h"])
     pre_traffic = load_traffic("prefill_fwd_gpt2_medium", pre_digest)
     dec_traffic = load_traffic("decode_paged_b64", dec_digest)
