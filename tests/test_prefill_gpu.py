@@ -99,6 +99,8 @@ D128 = [
     (1, 48, 6, 3001, 128, True, FP16),
     (2, 16, 2, 4160, 128, False, BF16),
     (2, 16, 4, 4100, 128, True, FP16),
+    (2, 16, 16, 4096, 128, True, BF16),   # one query head per kv head
+    (4, 32, 8, 2049, 128, True, BF16),    # the last 256-row tile holds one row
 ]
 
 
